@@ -1,0 +1,223 @@
+"""Decode-attention benchmark: µs per decode step and achieved HBM GB/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
+                    [--path bucketed|workqueue|nosplit|policy] [--kernel auto|valu|mfma]
+
+One step is the engine's device work for one decode step of one layer: the
+split kernel launch(es) and the merge launch(es) (or the single no-split
+launch), with the plan already resident on the GPU.  Inputs are generated
+(seeded, synthetic) and copied to HBM before timing.  To keep the 256 MB
+Infinity Cache from serving K/V, every step reads a different copy of the KV
+pools (as consecutive layers of a model would), with enough copies to exceed
+1 GiB.
+
+Printed JSON line: value = real-KV bytes (sum N_i * Hkv * d * 2 * 2) divided by
+the device step time measured with HIP events on the launch stream.  The
+roofline object reports the split kernel alone; cpu_baseline times the fp64
+CPU oracle on the same generated inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/step and achieved HBM GB/s (% of peak), paged GQA"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_PATH = {"tiny": "workqueue", "long": "bucketed", "bimodal": "workqueue",
+                "zipf": "workqueue", "uniform": "workqueue"}
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="long")
+    p.add_argument("--path", default=None)
+    p.add_argument("--splits", type=int, default=None)
+    p.add_argument("--kernel", default="auto")
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=15.0)
+    p.add_argument("--copies-gib", type=float, default=1.0,
+                   help="total size of the rotated KV pool copies")
+    return p.parse_args(argv)
+
+
+def describe(spec, path, splits, lens):
+    return (f"{spec.name}: B={spec.batch} Hq={spec.num_q_heads} Hkv={spec.num_kv_heads} "
+            f"d={spec.head_dim} P={spec.page_size} S={splits} {spec.dtype} path={path} "
+            f"N={'/'.join(str(int(n)) for n in lens) if len(lens) <= 8 else f'{len(lens)} rows'}")
+
+
+def time_engine(w, wd, path, splits, kernel, steps, warmup, copies_gib):
+    """Device-time a path; returns a dict of timings and counters."""
+    import torch
+
+    from paged_kv_gqa_block_amd import engine
+
+    prob = engine.problem_from_workload(w, kernel)
+    step = engine.DecodeStep(prob, path, splits)
+    stream = torch.cuda.current_stream()
+    info = step.plan(wd["seq_lens_host"], stream=stream)
+    pool_bytes = wd["k_pool"].numel() * 2 * 2
+    n_copies = max(1, min(64, math.ceil(copies_gib * (1 << 30) / pool_bytes)))
+    pools = [(wd["k_pool"], wd["v_pool"])]
+    for _ in range(n_copies - 1):
+        pools.append((wd["k_pool"].clone(), wd["v_pool"].clone()))
+    views = [dict(wd, k_pool=k, v_pool=v) for k, v in pools]
+    torch.cuda.synchronize()
+
+    for i in range(warmup):
+        step.run(views[i % n_copies], stream)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = ev[i]
+        v = views[(warmup + i) % n_copies]
+        e[0].record(stream)
+        step.decode(v, stream)
+        e[1].record(stream)
+        step.merge(stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+
+    # Synchronised wall time including policy-free host planning + H2D.
+    sync_us = []
+    for i in range(min(steps, 20)):
+        v = views[i % n_copies]
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        step.plan(wd["seq_lens_host"], stream=stream)
+        step.run(v, stream)
+        torch.cuda.synchronize()
+        sync_us.append((time.perf_counter() - t) * 1e6)
+
+    n_split = {0: info.n_buckets, 1: 1 if info.n_tasks else 0, 2: 1}[info.path]
+    return {
+        "info": info.as_dict(),
+        "n_split_launches": n_split,
+        "step_us_mean": 1e3 * statistics.fmean(step_ms),
+        "step_us_median": 1e3 * statistics.median(step_ms),
+        "split_us_mean": 1e3 * statistics.fmean(split_ms),
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "sync_wall_us_median": statistics.median(sync_us),
+        "n_copies": n_copies,
+        "out": step.out,
+    }
+
+
+def cpu_baseline(w, budget_s):
+    import numpy as np
+
+    import oracle
+    from paged_kv_gqa_block_amd import traces
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    a = traces.oracle_arrays(w)
+    spec = w["spec"]
+    lens = a["seq_lens"]
+    rows = list(range(spec.batch))
+    kv_row_bytes = [int(n) * spec.num_kv_heads * spec.head_dim * 2 * 2 for n in lens]
+    done_bytes, reps = 0, 0
+    t0 = time.perf_counter()
+    # Whole decode steps while within budget; at least one row.
+    while True:
+        for i in rows:
+            oracle.attention(a["q"], a["k_pool"], a["v_pool"], a["block_table"], lens,
+                             a["scale"], a["page_size"], a["dtype"], rows=[i])
+            done_bytes += kv_row_bytes[i]
+            if time.perf_counter() - t0 > budget_s:
+                break
+        reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle on the same {spec.name} inputs: {reps} pass(es) over "
+                      f"rows in order, {done_bytes / 1e6:.1f} MB of real KV in {dt:.1f} s "
+                      f"({os.cpu_count()} host cpus visible)",
+            "us_per_step_equiv": dt / max(done_bytes, 1) * sum(kv_row_bytes) * 1e6}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this engine runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path has no multi-GPU mode)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from paged_kv_gqa_block_amd import engine, traces
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    spec = traces.get_spec(args.config)
+    seed = traces.HELD_OUT_SEED if args.seed is None else args.seed
+    path = args.path or DEFAULT_PATH.get(args.config, "workqueue")
+    splits = args.splits or spec.splits
+    w = traces.generate(spec, seed)
+    lens = w["seq_lens"].numpy()
+    if path == "policy":
+        rules = engine.load_policy_table()
+        path, splits = engine.choose(rules, spec.batch, int(lens.max()))
+    wd = engine.to_device(w)
+    engine.validate_inputs(wd)
+
+    r = time_engine(w, wd, path, splits, args.kernel, args.steps, args.warmup, args.copies_gib)
+    info = r["info"]
+    kv = info["kv_bytes"]
+    gbs = kv / (r["step_us_mean"] * 1e-6) / 1e9
+    split_launch_us = r["split_us_mean"] / max(1, r["n_split_launches"])
+    split_gbs = (kv / max(1, r["n_split_launches"])) / (split_launch_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_ms_per_step"], 4),
+        "us_per_step": round(r["step_us_mean"], 2),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": describe(spec, path, splits, lens), "seed": seed,
+                   "kernel": args.kernel, "path": path, "splits": splits,
+                   "launches_per_step": info["n_launches"], "n_tasks": info["n_tasks"],
+                   "kv_bytes": kv, "merge_state_bytes": info["merge_state_bytes"],
+                   "pool_copies_rotated": r["n_copies"],
+                   "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1)},
+        "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "split decode", "launch_us": round(split_launch_us, 2)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

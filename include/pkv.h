@@ -1,0 +1,232 @@
+/*
+ * pkv.h -- C ABI of the paged grouped-query decode-attention engine for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the decode step of "PersistentKV: Page-Aware Decode
+ * Scheduling for Long-Context LLM Serving on Commodity GPUs" as summarised on
+ * its gist.science pages, section "Methodology / 1. Native block-table decode
+ * engine":
+ *   - GQA: G = Hq / Hkv query heads share one KV head (query head h reads KV
+ *     head h / G);
+ *   - Layout: the engine reads K and V pages in place through a block table
+ *     and never repacks them into contiguous tensors;
+ *   - Sequence splitting: each row's sequence is cut into S disjoint ranges,
+ *     each emitting a partial online-softmax state, and a separate merge
+ *     kernel combines those states exactly;
+ *   - Row-local bounds: real per-row lengths N_i (not padded ones) set the
+ *     page counts and split ranges; empty splits write a neutral state and
+ *     exit early;
+ *   - Compact workqueue: a 1-D grid over only the non-empty
+ *     (row, kv-head, split) intervals, instead of one launch pair per exact
+ *     length bucket.
+ * Section "2. Calibrated adaptive policy" picks the execution path from the
+ * batch size B and the longest context N_max with calibrated thresholds.
+ *
+ * Call order for one decode step of one layer:
+ *     pkv_policy -> pkv_plan -> pkv_decode -> pkv_merge (no merge for NOSPLIT)
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: every buffer is owned by the caller.  The library allocates
+ *     no device or host memory and keeps no global state; all functions are
+ *     re-entrant.
+ *   - Streams: GPU work is enqueued asynchronously on the given stream; the
+ *     library never synchronises.  A NULL stream is the default stream.
+ *   - Errors: a negative pkv_status is returned and nothing is enqueued.
+ *     Arguments are validated on the host before any launch.  Block-table
+ *     entries are not read on the host: an entry outside [0, num_pool_pages)
+ *     among a row's first ceil(N_i / P) entries is undefined behaviour.
+ *   - Layouts (all row-major, contiguous, element type = problem dtype
+ *     unless stated):
+ *       q, out          [B][Hq][d]
+ *       k_pool, v_pool  [num_pool_pages][Hkv][P][d]   (one KV head's page is
+ *                                                       one contiguous P*d run)
+ *       block_table     int32 [B][max_pages_per_row]; entry j of row i is the
+ *                       pool page holding tokens [j*P, (j+1)*P) of row i
+ *       seq_lens        int32 [B], 0 <= N_i <= max_pages_per_row * P
+ *       lse             float32 [B][Hq], natural-log sum of exp of the scaled
+ *                       scores (-inf for an empty row)
+ *       st_m, st_l      float32 [n_state_slots][G]    running max and sum of
+ *                                                      exp(score - max)
+ *       st_o            float32 [n_state_slots][G][d] unnormalised output
+ *     A score is sm_scale * <q_h, k_t>.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1, /* null pointer, bad enum, non-positive size            */
+  PKV_ESHAPE = -2, /* unsupported shape: Hq % Hkv, d, P, G, plan mismatch  */
+  PKV_EDTYPE = -3, /* unsupported dtype                                    */
+  PKV_ERANGE = -4, /* a length or split count out of range; no policy rule */
+  PKV_ENOSPC = -5, /* plan buffer too small                                */
+  PKV_EHIP = -6    /* a HIP call or kernel launch failed                   */
+};
+
+enum { PKV_F16 = 0, PKV_BF16 = 1 };
+
+/* Execution paths (policy output, plan input). */
+enum {
+  PKV_BUCKETED = 0,  /* exact-length buckets: per bucket one rectangular
+                        rows x Hkv x S split grid and one merge launch      */
+  PKV_WORKQUEUE = 1, /* compact 1-D workqueue of non-empty tasks + 1 merge  */
+  PKV_NOSPLIT = 2    /* one single-pass launch, one workgroup per
+                        (row, kv head), writes the normalised output        */
+};
+
+/* Split-kernel arithmetic. AUTO picks the faster one measured on MI355X. */
+enum { PKV_KERNEL_AUTO = 0, PKV_KERNEL_VALU = 1, PKV_KERNEL_MFMA = 2 };
+
+typedef struct pkv_problem {
+  int32_t batch;             /* B >= 1                                        */
+  int32_t num_q_heads;       /* Hq >= 1                                       */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0, G = Hq/Hkv <= 16     */
+  int32_t head_dim;          /* d: 64 or 128                                  */
+  int32_t page_size;         /* P: 16 tokens per page                         */
+  int32_t num_pool_pages;    /* pages in each of the K and V pools, >= 1      */
+  int32_t max_pages_per_row; /* block-table row stride, >= 1                  */
+  int32_t dtype;             /* PKV_F16 or PKV_BF16 (q, pools and out)        */
+  float sm_scale;            /* softmax scale, e.g. 1/sqrt(d)                 */
+  int32_t kernel;            /* PKV_KERNEL_*                                  */
+} pkv_problem;
+
+/* Workload counters of one plan (the scheduler-derived counters of the
+ * pages' evaluation: tasks, launches per step, merge-state traffic). */
+typedef struct pkv_plan_info {
+  int32_t path;
+  int32_t n_tasks;          /* non-empty (row, kv head, split) tasks        */
+  int32_t n_buckets;        /* exact-length buckets (BUCKETED), else 0      */
+  int32_t n_launches;       /* kernel launches per step (split + merge)     */
+  int32_t n_state_slots;    /* partial-state slots written by the split     */
+  int32_t n_empty_slots;    /* slots that only hold a neutral state         */
+  int32_t splits;           /* S, the split cap per row                     */
+  int32_t pages_per_split;  /* WORKQUEUE granule (pages), else 0            */
+  int64_t kv_bytes;         /* bytes of real KV tokens: sum N_i*Hkv*d*2*e   */
+  int64_t merge_state_bytes;/* 2 * slots * G * (d + 2) * 4: written + read  */
+  int64_t plan_bytes;       /* bytes of the plan buffer actually used       */
+} pkv_plan_info;
+
+/* Ordered policy rules, first match wins.  Row r is
+ *   rules[6*r .. 6*r+5] = { b_lo, b_hi, nmax_lo, nmax_hi, path, splits }
+ * and matches when b_lo <= B <= b_hi and nmax_lo <= N_max <= nmax_hi. */
+typedef struct pkv_policy_table {
+  int32_t n_rules;
+  const int32_t* rules;
+} pkv_policy_table;
+
+/*
+ * Plan buffer (int32 words, written by pkv_plan; callers may read it):
+ *   [0]  magic 0x31564B50 ("PKV1")     [1]  path
+ *   [2]  batch                          [3]  num_kv_heads
+ *   [4]  splits S                       [5]  pages_per_split (WORKQUEUE)
+ *   [6]  n_tasks                        [7]  n_buckets
+ *   [8]  n_state_slots                  [9]  n_empty_slots
+ *   [10] word offset of tasks           [11] word offset of buckets
+ *   [12] word offset of bucket rows     [13] total words used
+ *   [14] page_size                      [15] group G
+ *   [16 ..]            row_len[B]       (N_i)
+ *   [16+B ..]          row_pages[B]     (T_i = ceil(N_i / P))
+ *   [16+2B ..]         row_nsplit[B]
+ *   [16+3B ..]         row_task_off[B+1] (first task of each row in task
+ *                      order; entry B = n_tasks)
+ *   tasks[n_tasks][4]  { row, (kv_head << 16) | split, page_begin, page_end }
+ *                      starting at word [10], a multiple of 4
+ *                      ordered (row, kv_head, split); WORKQUEUE: the state
+ *                      slot of task j is j
+ *   buckets[n_buckets][8] { length, pages, pages_per_split, nsplit, n_rows,
+ *                           first index into bucket rows, 0, 0 }
+ *                      ascending length; BUCKETED state slot of
+ *                      (row, kv_head, split) is (row * Hkv + kv_head) * S + split
+ *   bucket_rows[B]     rows of every bucket, bucket-major, ascending inside
+ * Split s of a row covers pages [page_begin, page_end) and tokens
+ * [page_begin * P, min(page_end * P, N_i)).
+ */
+#define PKV_PLAN_MAGIC 0x31564B50
+#define PKV_PLAN_HEADER_WORDS 16
+
+/* Upper bound, in bytes, of the plan buffer for this problem, path and
+ * split cap.  Returns 0 on invalid arguments. */
+size_t pkv_plan_bytes(const pkv_problem* prob, int32_t path, int32_t max_splits);
+
+/*
+ * Build the plan on the host from the host copy of the row lengths, write it
+ * to plan_host and, when plan_dev is not NULL, enqueue one host-to-device
+ * copy of the used bytes on `stream` (plan_host should then be pinned and
+ * must stay unchanged until the copy has run).  Split rules (row-local
+ * bounds, see the header comment):
+ *   WORKQUEUE: pps = max(1, ceil(T_max / S)) pages, shared by the batch; row i
+ *              gets ceil(T_i / pps) splits; tasks only for non-empty splits.
+ *   BUCKETED:  rows grouped by exact length; bucket b uses
+ *              pps_b = max(1, ceil(T_b / S)) and ceil(T_b / pps_b) splits;
+ *              its grid has rows_b * Hkv * S slots, the rest neutral.
+ *   NOSPLIT:   one task per (row, kv head) of every non-empty row.
+ * Errors: PKV_EINVAL (null pointer, max_splits < 1 or > 65535, bad path),
+ * PKV_ESHAPE (problem shape), PKV_ERANGE (N_i < 0 or N_i > max_pages_per_row*P),
+ * PKV_ENOSPC (plan_bytes too small), PKV_EHIP (the copy failed to enqueue).
+ * info_out may be NULL.
+ */
+pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_host, int32_t path,
+                    int32_t max_splits, void* plan_host, void* plan_dev, size_t plan_bytes,
+                    pkv_plan_info* info_out, hipStream_t stream);
+
+/* Counters of an existing plan (reads plan_host only). */
+pkv_status pkv_plan_get_info(const pkv_problem* prob, const void* plan_host,
+                             pkv_plan_info* info_out);
+
+/*
+ * Split decode (the engine's first kernel, or the whole step for NOSPLIT).
+ * plan_host is read for launch shapes; plan_dev (the device copy of the same
+ * plan, already enqueued on `stream`) is read by the kernels.
+ *   WORKQUEUE / BUCKETED: writes st_m, st_l, st_o for all n_state_slots
+ *     slots (neutral (-inf, 0, 0) for empty slots); out and lse are unused.
+ *   NOSPLIT: writes out (and lse when not NULL) for every row; st_* unused
+ *     and may be NULL.  Rows with N_i = 0 get out = 0, lse = -inf.
+ * Tokens past N_i in a row's last page, and pool pages not referenced by the
+ * first T_i table entries of a row, are never used (they may hold NaN).
+ * Errors: PKV_EINVAL, PKV_ESHAPE (shape or plan/problem mismatch),
+ * PKV_EDTYPE, PKV_EHIP.
+ */
+pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host, const void* plan_dev,
+                      const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens_dev, float* st_m,
+                      float* st_l, float* st_o, void* out, float* lse, hipStream_t stream);
+
+/*
+ * Merge (the engine's second kernel): for each (row, q head) combine the
+ * row's partial states exactly: M = max_s m_s, w_s = exp(m_s - M),
+ * L = sum_s w_s l_s, out = sum_s w_s o_s / L rounded to nearest-even into the
+ * problem dtype, lse = M + ln L.  All-neutral rows give out = 0, lse = -inf.
+ * WORKQUEUE: one launch; BUCKETED: one launch per bucket; NOSPLIT: no-op.
+ * lse may be NULL.  Errors as pkv_decode.
+ */
+pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void* plan_dev,
+                     const float* st_m, const float* st_l, const float* st_o, void* out,
+                     float* lse, hipStream_t stream);
+
+/*
+ * Calibrated path choice: first rule of `table` matching (batch, max_len).
+ * Writes the rule's path and split cap.  Errors: PKV_EINVAL (null pointer,
+ * negative n_rules, a rule with an unknown path or splits < 1),
+ * PKV_ERANGE (no rule matches; outputs untouched).
+ */
+pkv_status pkv_policy(const pkv_policy_table* table, int32_t batch, int32_t max_len,
+                      int32_t* path_out, int32_t* splits_out);
+
+/* Static description of a status code; never NULL. */
+const char* pkv_status_str(pkv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,249 @@
+"""ctypes binding of libpkv.so (include/pkv.h).
+
+Argument marshalling only: every step of the decode path runs in the
+library's host planner and HIP kernels.  torch tensors are accepted wherever
+the C ABI takes a pointer (their ``data_ptr()`` is passed); numpy arrays are
+accepted for host buffers.  A missing or stale library raises at import of
+this module -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+# torch ships its own HIP runtime (libamdhip64, soname libamdhip64.so.7).  It
+# must be the one libpkv binds to: importing torch first makes the dynamic
+# loader resolve libpkv's libamdhip64.so.7 to torch's already-loaded copy, so
+# device pointers and streams from torch are valid inside the library.  If
+# libpkv were loaded first, torch would load a second runtime.
+import torch  # noqa: F401  (load order matters, see above)
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE, PKV_ENOSPC, PKV_EHIP = 0, -1, -2, -3, -4, -5, -6
+PKV_F16, PKV_BF16 = 0, 1
+PKV_BUCKETED, PKV_WORKQUEUE, PKV_NOSPLIT = 0, 1, 2
+PKV_KERNEL_AUTO, PKV_KERNEL_VALU, PKV_KERNEL_MFMA = 0, 1, 2
+PKV_PLAN_MAGIC = 0x31564B50
+PKV_PLAN_HEADER_WORDS = 16
+
+PATH_NAMES = {PKV_BUCKETED: "bucketed", PKV_WORKQUEUE: "workqueue", PKV_NOSPLIT: "nosplit"}
+PATH_IDS = {v: k for k, v in PATH_NAMES.items()}
+DTYPE_IDS = {"f16": PKV_F16, "bf16": PKV_BF16}
+KERNEL_IDS = {"auto": PKV_KERNEL_AUTO, "valu": PKV_KERNEL_VALU, "mfma": PKV_KERNEL_MFMA}
+
+EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pkv_merge",
+            "pkv_policy", "pkv_status_str")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+class pkv_problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pool_pages", ctypes.c_int32),
+        ("max_pages_per_row", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("kernel", ctypes.c_int32),
+    ]
+
+
+class pkv_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int32),
+        ("n_tasks", ctypes.c_int32),
+        ("n_buckets", ctypes.c_int32),
+        ("n_launches", ctypes.c_int32),
+        ("n_state_slots", ctypes.c_int32),
+        ("n_empty_slots", ctypes.c_int32),
+        ("splits", ctypes.c_int32),
+        ("pages_per_split", ctypes.c_int32),
+        ("kv_bytes", ctypes.c_int64),
+        ("merge_state_bytes", ctypes.c_int64),
+        ("plan_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class pkv_policy_table(ctypes.Structure):
+    _fields_ = [("n_rules", ctypes.c_int32), ("rules", ctypes.POINTER(ctypes.c_int32))]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m paged_kv_gqa_block_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    _check_single_hip_runtime()
+    vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_float)
+    prob_p = ctypes.POINTER(pkv_problem)
+    lib.pkv_plan_bytes.argtypes = [prob_p, i32, i32]
+    lib.pkv_plan_bytes.restype = ctypes.c_size_t
+    lib.pkv_plan.argtypes = [prob_p, vp, i32, i32, vp, vp, ctypes.c_size_t,
+                             ctypes.POINTER(pkv_plan_info), vp]
+    lib.pkv_plan.restype = i32
+    lib.pkv_plan_get_info.argtypes = [prob_p, vp, ctypes.POINTER(pkv_plan_info)]
+    lib.pkv_plan_get_info.restype = i32
+    lib.pkv_decode.argtypes = [prob_p, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.pkv_decode.restype = i32
+    lib.pkv_merge.argtypes = [prob_p, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.pkv_merge.restype = i32
+    lib.pkv_policy.argtypes = [ctypes.POINTER(pkv_policy_table), i32, i32,
+                               ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.pkv_policy.restype = i32
+    lib.pkv_status_str.argtypes = [i32]
+    lib.pkv_status_str.restype = ctypes.c_char_p
+    del f32p
+    return lib
+
+
+def _check_single_hip_runtime() -> None:
+    """Fail loudly if two different libamdhip64 copies are mapped."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:  # pragma: no cover
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise ImportError(f"two HIP runtimes loaded: {sorted(real)}")
+
+
+LIB = _load()
+
+
+def pkv_status_str(status: int) -> str:
+    return LIB.pkv_status_str(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PKV_OK:
+        raise PkvError(fn, status, pkv_status_str(status))
+
+
+def _ptr(x) -> int | None:
+    """Address of a torch tensor / numpy array / raw int; None stays NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        assert x.flags["C_CONTIGUOUS"]
+        return x.ctypes.data
+    assert x.is_contiguous(), "tensors passed to libpkv must be contiguous"
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_problem(batch, num_q_heads, num_kv_heads, head_dim, page_size, num_pool_pages,
+                 max_pages_per_row, dtype="f16", sm_scale=None, kernel="auto") -> pkv_problem:
+    if sm_scale is None:
+        sm_scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+    return pkv_problem(batch, num_q_heads, num_kv_heads, head_dim, page_size, num_pool_pages,
+                       max_pages_per_row, DTYPE_IDS.get(dtype, dtype) if isinstance(dtype, str)
+                       else dtype, sm_scale, KERNEL_IDS[kernel] if isinstance(kernel, str)
+                       else kernel)
+
+
+def pkv_plan_bytes(prob: pkv_problem, path: int, max_splits: int) -> int:
+    return LIB.pkv_plan_bytes(ctypes.byref(prob), path, max_splits)
+
+
+def pkv_plan(prob: pkv_problem, seq_lens_host, path: int, max_splits: int, plan_host,
+             plan_dev=None, plan_bytes: int | None = None, stream=None) -> pkv_plan_info:
+    info = pkv_plan_info()
+    if plan_bytes is None:
+        plan_bytes = plan_host.numel() * plan_host.element_size() if hasattr(
+            plan_host, "numel") else plan_host.nbytes
+    seq = seq_lens_host
+    if isinstance(seq, np.ndarray):
+        assert seq.dtype == np.int32 and seq.flags["C_CONTIGUOUS"]
+    else:
+        assert str(seq.dtype) == "torch.int32" and seq.device.type == "cpu"
+    _check("pkv_plan", LIB.pkv_plan(ctypes.byref(prob), _ptr(seq), path, max_splits,
+                                    _ptr(plan_host), _ptr(plan_dev), plan_bytes,
+                                    ctypes.byref(info), _stream(stream)))
+    return info
+
+
+def pkv_plan_get_info(prob: pkv_problem, plan_host) -> pkv_plan_info:
+    info = pkv_plan_info()
+    _check("pkv_plan_get_info",
+           LIB.pkv_plan_get_info(ctypes.byref(prob), _ptr(plan_host), ctypes.byref(info)))
+    return info
+
+
+def pkv_decode(prob: pkv_problem, plan_host, plan_dev, q, k_pool, v_pool, block_table,
+               seq_lens_dev, st_m=None, st_l=None, st_o=None, out=None, lse=None,
+               stream=None) -> None:
+    _check("pkv_decode", LIB.pkv_decode(
+        ctypes.byref(prob), _ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k_pool),
+        _ptr(v_pool), _ptr(block_table), _ptr(seq_lens_dev), _ptr(st_m), _ptr(st_l),
+        _ptr(st_o), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def pkv_merge(prob: pkv_problem, plan_host, plan_dev, st_m, st_l, st_o, out, lse=None,
+              stream=None) -> None:
+    _check("pkv_merge", LIB.pkv_merge(
+        ctypes.byref(prob), _ptr(plan_host), _ptr(plan_dev), _ptr(st_m), _ptr(st_l),
+        _ptr(st_o), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def pkv_policy(rules, batch: int, max_len: int):
+    """rules: sequence of (b_lo, b_hi, nmax_lo, nmax_hi, path_id, splits)."""
+    flat = np.ascontiguousarray(np.asarray(rules, dtype=np.int32).reshape(-1))
+    table = pkv_policy_table(len(flat) // 6,
+                             flat.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    path, splits = ctypes.c_int32(), ctypes.c_int32()
+    _check("pkv_policy", LIB.pkv_policy(ctypes.byref(table), batch, max_len,
+                                        ctypes.byref(path), ctypes.byref(splits)))
+    return path.value, splits.value
+
+
+def decode_plan(plan_host) -> dict:
+    """Read a plan buffer (layout in include/pkv.h) into Python lists."""
+    w = np.asarray(plan_host.numpy() if hasattr(plan_host, "numpy") else plan_host).view(np.int32)
+    assert w[0] == PKV_PLAN_MAGIC
+    b = int(w[2])
+    h = PKV_PLAN_HEADER_WORDS
+    n_tasks, n_buckets = int(w[6]), int(w[7])
+    ot, ob, obr = int(w[10]), int(w[11]), int(w[12])
+    tasks = w[ot:ot + 4 * n_tasks].reshape(-1, 4)
+    return {
+        "path": PATH_NAMES[int(w[1])],
+        "batch": b,
+        "splits": int(w[4]),
+        "pages_per_split": int(w[5]),
+        "n_state_slots": int(w[8]),
+        "n_empty_slots": int(w[9]),
+        "row_len": w[h:h + b].tolist(),
+        "row_pages": w[h + b:h + 2 * b].tolist(),
+        "row_nsplit": w[h + 2 * b:h + 3 * b].tolist(),
+        "row_task_off": w[h + 3 * b:h + 4 * b + 1].tolist(),
+        "tasks": [(int(t[0]), int(t[1]) >> 16, int(t[1]) & 0xFFFF, int(t[2]), int(t[3]))
+                  for t in tasks],
+        "buckets": [tuple(int(x) for x in w[ob + 8 * k:ob + 8 * k + 8]) for k in range(n_buckets)],
+        "bucket_rows": w[obr:obr + b].tolist() if n_buckets else [],
+        "total_words": int(w[13]),
+    }

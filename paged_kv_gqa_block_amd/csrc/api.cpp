@@ -1,0 +1,168 @@
+// Public entry points pkv_decode, pkv_merge, pkv_policy and pkv_status_str:
+// argument validation on the host, then kernel launches on the caller's
+// stream.  The planner entry points live in planner.cpp.
+#include <cmath>
+
+#include "pkv_internal.h"
+
+using namespace pkv;
+
+namespace {
+
+// Checks that the plan in plan_host was made for this problem; returns its
+// header words through `w`.
+pkv_status check_plan(const pkv_problem* prob, const void* plan_host, const int32_t** w_out) {
+  if (!plan_host) return PKV_EINVAL;
+  const int32_t* w = static_cast<const int32_t*>(plan_host);
+  if (w[kMagic] != PKV_PLAN_MAGIC) return PKV_EINVAL;
+  if (w[kBatch] != prob->batch || w[kNumKvHeads] != prob->num_kv_heads ||
+      w[kWordPageSize] != prob->page_size || w[kWordGroup] != prob->num_q_heads / prob->num_kv_heads)
+    return PKV_ESHAPE;
+  if (w[kPath] < PKV_BUCKETED || w[kPath] > PKV_NOSPLIT) return PKV_EINVAL;
+  *w_out = w;
+  return PKV_OK;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
+                                 const void* plan_dev, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_table,
+                                 const int32_t* seq_lens_dev, float* st_m, float* st_l,
+                                 float* st_o, void* out, float* lse, hipStream_t stream) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  const int32_t* w = nullptr;
+  st = check_plan(prob, plan_host, &w);
+  if (st != PKV_OK) return st;
+  if (!plan_dev || !q || !k_pool || !v_pool || !block_table || !seq_lens_dev) return PKV_EINVAL;
+  const int path = w[kPath];
+  if (path == PKV_NOSPLIT) {
+    if (!out) return PKV_EINVAL;
+  } else if (w[kNumStateSlots] > 0 && (!st_m || !st_l || !st_o)) {
+    return PKV_EINVAL;
+  }
+
+  SplitArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens_dev;
+  a.st_m = st_m;
+  a.st_l = st_l;
+  a.st_o = st_o;
+  a.out = out;
+  a.lse = lse;
+  a.num_q_heads = prob->num_q_heads;
+  a.num_kv_heads = prob->num_kv_heads;
+  a.max_pages = prob->max_pages_per_row;
+  a.splits = w[kSplits];
+  a.scale_log2 = prob->sm_scale * kLog2e;
+  const int32_t* dev = static_cast<const int32_t*>(plan_dev);
+
+  if (path == PKV_WORKQUEUE) {
+    const int n = w[kNumTasks];
+    if (n == 0) return PKV_OK;
+    a.tasks = dev + w[kOffTasks];
+    a.num_items = n;
+    return launch_split(*prob, kModeWorkqueue, prob->kernel, a, n, stream);
+  }
+  if (path == PKV_NOSPLIT) {
+    const int n = prob->batch * prob->num_kv_heads;
+    a.num_items = n;
+    return launch_split(*prob, kModeNoSplit, prob->kernel, a, n, stream);
+  }
+  // BUCKETED: one rectangular rows_b x Hkv x S launch per exact-length bucket.
+  const int32_t* bw = w + w[kOffBuckets];
+  for (int k = 0; k < w[kNumBuckets]; ++k) {
+    const int32_t* e = bw + kBucketWords * k;
+    const int64_t items = int64_t(e[4]) * prob->num_kv_heads * w[kSplits];
+    if (items > INT32_MAX) return PKV_ERANGE;
+    a.bucket_pages = e[1];
+    a.bucket_pps = e[2];
+    a.bucket_nsplit = e[3];
+    a.bucket_rows = dev + w[kOffBucketRows] + e[5];
+    a.num_items = static_cast<int32_t>(items);
+    st = launch_split(*prob, kModeBucket, prob->kernel, a, static_cast<int>(items), stream);
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host,
+                                const void* plan_dev, const float* st_m, const float* st_l,
+                                const float* st_o, void* out, float* lse, hipStream_t stream) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  const int32_t* w = nullptr;
+  st = check_plan(prob, plan_host, &w);
+  if (st != PKV_OK) return st;
+  const int path = w[kPath];
+  if (path == PKV_NOSPLIT) return PKV_OK;
+  if (!plan_dev || !out) return PKV_EINVAL;
+  if (w[kNumStateSlots] > 0 && (!st_m || !st_l || !st_o)) return PKV_EINVAL;
+  const int32_t* dev = static_cast<const int32_t*>(plan_dev);
+  const int b = prob->batch;
+
+  MergeArgs a{};
+  a.st_m = st_m;
+  a.st_l = st_l;
+  a.st_o = st_o;
+  a.out = out;
+  a.lse = lse;
+  a.num_q_heads = prob->num_q_heads;
+  a.num_kv_heads = prob->num_kv_heads;
+  a.splits = w[kSplits];
+  if (path == PKV_WORKQUEUE) {
+    a.row_nsplit = dev + PKV_PLAN_HEADER_WORDS + 2 * b;
+    a.row_task_off = dev + PKV_PLAN_HEADER_WORDS + 3 * b;
+    a.num_rows = b;
+    a.mode = kModeWorkqueue;
+    return launch_merge(*prob, a, stream);
+  }
+  const int32_t* bw = w + w[kOffBuckets];
+  for (int k = 0; k < w[kNumBuckets]; ++k) {
+    const int32_t* e = bw + kBucketWords * k;
+    a.bucket_rows = dev + w[kOffBucketRows] + e[5];
+    a.num_rows = e[4];
+    a.mode = kModeBucket;
+    st = launch_merge(*prob, a, stream);
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_policy(const pkv_policy_table* table, int32_t batch, int32_t max_len,
+                                 int32_t* path_out, int32_t* splits_out) {
+  if (!table || !path_out || !splits_out || table->n_rules < 0) return PKV_EINVAL;
+  if (table->n_rules > 0 && !table->rules) return PKV_EINVAL;
+  for (int r = 0; r < table->n_rules; ++r) {
+    const int32_t* e = table->rules + 6 * r;
+    if (e[4] < PKV_BUCKETED || e[4] > PKV_NOSPLIT || e[5] < 1) return PKV_EINVAL;
+  }
+  for (int r = 0; r < table->n_rules; ++r) {
+    const int32_t* e = table->rules + 6 * r;
+    if (e[0] <= batch && batch <= e[1] && e[2] <= max_len && max_len <= e[3]) {
+      *path_out = e[4];
+      *splits_out = e[5];
+      return PKV_OK;
+    }
+  }
+  return PKV_ERANGE;
+}
+
+extern "C" const char* pkv_status_str(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_ESHAPE: return "unsupported or mismatched shape";
+    case PKV_EDTYPE: return "unsupported dtype";
+    case PKV_ERANGE: return "value out of range";
+    case PKV_ENOSPC: return "plan buffer too small";
+    case PKV_EHIP: return "HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,89 @@
+// Internal declarations shared by the host planner, the API layer and the
+// kernel launchers of libpkv.  Not part of the public ABI (see include/pkv.h).
+#pragma once
+
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Word offsets inside the plan header (layout documented in pkv.h).
+enum PlanWord : int {
+  kMagic = 0,
+  kPath = 1,
+  kBatch = 2,
+  kNumKvHeads = 3,
+  kSplits = 4,
+  kPagesPerSplit = 5,
+  kNumTasks = 6,
+  kNumBuckets = 7,
+  kNumStateSlots = 8,
+  kNumEmptySlots = 9,
+  kOffTasks = 10,
+  kOffBuckets = 11,
+  kOffBucketRows = 12,
+  kTotalWords = 13,
+  kWordPageSize = 14,
+  kWordGroup = 15,
+};
+
+constexpr int kBucketWords = 8;
+constexpr int kTaskWords = 4;
+constexpr int kPageSize = 16;
+constexpr int kMaxGroup = 16;
+
+// Which grid a split-kernel launch walks.
+enum SplitMode : int { kModeWorkqueue = 0, kModeBucket = 1, kModeNoSplit = 2 };
+
+// Everything a split / no-split kernel needs; passed by value as a kernel
+// argument.  Pointers are device pointers.
+struct SplitArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* tasks;        // workqueue: tasks[n][4]
+  const int32_t* bucket_rows;  // bucket: rows of this bucket
+  float* st_m;
+  float* st_l;
+  float* st_o;
+  void* out;    // no-split
+  float* lse;   // no-split, may be null
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_pages;  // block-table row stride
+  int32_t splits;     // bucket: S (slot stride)
+  int32_t bucket_pps;
+  int32_t bucket_nsplit;
+  int32_t bucket_pages;
+  int32_t num_items;  // grid items (tasks, bucket slots or rows * Hkv)
+  float scale_log2;   // sm_scale * log2(e)
+};
+
+struct MergeArgs {
+  const float* st_m;
+  const float* st_l;
+  const float* st_o;
+  const int32_t* row_nsplit;    // workqueue
+  const int32_t* row_task_off;  // workqueue
+  const int32_t* bucket_rows;   // bucket: rows of this bucket
+  void* out;
+  float* lse;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t splits;     // bucket slot stride S
+  int32_t num_rows;   // rows covered by this launch
+  int32_t mode;       // kModeWorkqueue or kModeBucket
+};
+
+// Kernel launchers (HIP translation units).  Return PKV_OK or PKV_EHIP.
+pkv_status launch_split(const pkv_problem& prob, int mode, int kernel, const SplitArgs& args,
+                        int grid, hipStream_t stream);
+pkv_status launch_merge(const pkv_problem& prob, const MergeArgs& args, hipStream_t stream);
+
+// Shape checks shared by plan / decode / merge.
+pkv_status check_problem(const pkv_problem* prob);
+
+}  // namespace pkv

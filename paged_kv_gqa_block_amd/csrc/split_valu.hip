@@ -1,0 +1,308 @@
+// Split / no-split decode kernel, vector-ALU variant (gfx950).
+//
+// One workgroup per task (row, kv head, page range).  The pages of the task
+// are dealt round-robin to the workgroup's waves; a wave reads one whole KV
+// page per step with coalesced 16-byte loads (one wave-wide load covers
+// 1 KiB, i.e. 64/(d/8) tokens), and keeps the next page in flight while it
+// computes the current one.  Lane layout after a load: the d/8 lanes of a
+// "stream" hold one token row, 8 elements each; a wave holds 64/(d/8)
+// streams.  Scores are packed dot products (v_dot2) reduced across the
+// stream's lanes with DPP; every stream keeps its own running max / sum /
+// unnormalised output (online softmax), so no cross-stream traffic happens
+// per page.  Streams are merged inside the wave, waves through LDS, and the
+// workgroup writes either the partial state (split paths) or the normalised
+// output (no-split path).
+//
+// Method: PersistentKV summary pages, "Methodology / 1. Native block-table
+// decode engine" (GQA over paged KV read through the block table, partial
+// online-softmax state per disjoint split, empty splits write neutral state).
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+template <int D, int GP, bool BF16, int NW, int MODE>
+__global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
+  constexpr int CPT = D / 8;     // 16-byte chunks per token row
+  constexpr int TPI = 64 / CPT;  // tokens per wave-wide 16-byte load
+  constexpr int NL = 16 / TPI;   // loads per page (16 tokens per page)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane % CPT;  // chunk: elements [8c, 8c+8)
+  const int r = lane / CPT;  // stream: tokens r, r+TPI, ... of each page
+  const int hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / hkv;  // real heads in the group (<= GP)
+
+  __shared__ float sm_m[NW][GP];
+  __shared__ float sm_l[NW][GP];
+  __shared__ float sm_o[NW][GP][D];
+
+  // ---- task --------------------------------------------------------------
+  const int item = blockIdx.x;
+  int row, g, pb, pe;
+  int64_t slot = 0;
+  if constexpr (MODE == kModeWorkqueue) {
+    const int4 t = reinterpret_cast<const int4*>(a.tasks)[item];
+    row = t.x;
+    g = t.y >> 16;
+    pb = t.z;
+    pe = t.w;
+    slot = item;
+  } else if constexpr (MODE == kModeBucket) {
+    const int s = item % a.splits;
+    const int rest = item / a.splits;
+    g = rest % hkv;
+    row = a.bucket_rows[rest / hkv];
+    slot = (int64_t(row) * hkv + g) * a.splits + s;
+    if (s >= a.bucket_nsplit) {  // empty split: neutral state, exit early
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) a.st_o[slot * G * D + e] = 0.f;
+      if (threadIdx.x < G) {
+        a.st_m[slot * G + threadIdx.x] = kNegInf;
+        a.st_l[slot * G + threadIdx.x] = 0.f;
+      }
+      return;
+    }
+    pb = s * a.bucket_pps;
+    pe = min(pb + a.bucket_pps, a.bucket_pages);
+  } else {
+    row = item / hkv;
+    g = item % hkv;
+    pb = 0;
+    pe = 0;
+  }
+  const int n = a.seq_lens[row];
+  if constexpr (MODE == kModeNoSplit) {
+    pe = (n + 15) >> 4;
+    if (pe == 0) {  // empty row: zero output, lse = -inf
+      uint16_t* out = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.num_q_heads + g * G) * D;
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) out[e] = 0;
+      if (a.lse && threadIdx.x < G) a.lse[int64_t(row) * a.num_q_heads + g * G + threadIdx.x] =
+          kNegInf;
+      return;
+    }
+  }
+
+  // ---- query: GP heads x 8 elements per lane ------------------------------
+  uint4 qv[GP];
+  {
+    const uint16_t* qp =
+        static_cast<const uint16_t*>(a.q) + (int64_t(row) * a.num_q_heads + g * G) * D + 8 * c;
+#pragma unroll
+    for (int h = 0; h < GP; ++h) qv[h] = (h < G) ? load16(qp + h * D) : zero4();
+  }
+
+  float m[GP], l[GP], o[GP][8];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    m[h] = kNegInf;
+    l[h] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
+  }
+
+  const int64_t page_stride = int64_t(hkv) * 16 * D;  // elements
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + int64_t(g) * 16 * D + 8 * lane;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + int64_t(g) * 16 * D + 8 * lane;
+  const int32_t* bt = a.block_table + int64_t(row) * a.max_pages;
+  const float sl2 = a.scale_log2;
+
+  const int first = pb + wave;
+  const int cnt = (pe > first) ? (pe - first + NW - 1) / NW : 0;
+
+  auto load_page = [&](int k, uint4 (&kk)[NL], uint4 (&vv)[NL]) {
+    const int pg = first + k * NW;
+    const int pid = bt[pg];
+    const uint16_t* kp = kbase + int64_t(pid) * page_stride;
+    const uint16_t* vp = vbase + int64_t(pid) * page_stride;
+    const int valid = n - pg * 16;  // real tokens in this page (>= 1)
+    if (valid >= 16) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        kk[i] = load16(kp + i * 512);
+        vv[i] = load16(vp + i * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const bool ok = i * TPI + r < valid;
+        kk[i] = ok ? load16(kp + i * 512) : zero4();
+        vv[i] = ok ? load16(vp + i * 512) : zero4();
+      }
+    }
+  };
+
+  auto compute_page = [&](int k, const uint4 (&kk)[NL], const uint4 (&vv)[NL]) {
+    const int valid = n - (first + k * NW) * 16;
+    float x[NL][GP];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int h = 0; h < GP; ++h) x[i][h] = group_sum<CPT>(dot8<BF16>(kk[i], qv[h], 0.f)) * sl2;
+    float vf[NL][8];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vf[i][2 * j] = Elem<BF16>::lo(w[j]);
+        vf[i][2 * j + 1] = Elem<BF16>::hi(w[j]);
+      }
+    }
+    const bool tail = valid < 16;  // wave-uniform
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if (i * TPI + r >= valid)
+#pragma unroll
+          for (int h = 0; h < GP; ++h) x[i][h] = kNegInf;
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      float mp = x[0][h];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) mp = fmaxf(mp, x[i][h]);
+      const float mn = fmaxf(m[h], mp);
+      // A stream that has only seen masked tokens keeps m = -inf; use 0 as
+      // the exponent base so that exp2(-inf - base) = 0 instead of NaN.
+      const float base = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m[h] - base);
+      m[h] = mn;
+      float lh = l[h] * alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[h][j] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float p = fast_exp2(x[i][h] - base);
+        lh += p;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[h][j] = fmaf(p, vf[i][j], o[h][j]);
+      }
+      l[h] = lh;
+    }
+  };
+
+  if (cnt > 0) {
+    uint4 kc[NL], vc[NL];
+    load_page(0, kc, vc);
+    for (int k = 0; k < cnt; ++k) {
+      uint4 kn[NL], vn[NL];
+      if (k + 1 < cnt) load_page(k + 1, kn, vn);
+      compute_page(k, kc, vc);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        kc[i] = kn[i];
+        vc[i] = vn[i];
+      }
+    }
+  }
+
+  // ---- merge the wave's streams (lanes r = 0 .. TPI-1) ---------------------
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    float mx = m[h];
+#pragma unroll
+    for (int sh = CPT; sh < 64; sh <<= 1) mx = fmaxf(mx, shfl_xor(mx, sh));
+    const float wgt = (m[h] == kNegInf) ? 0.f : fast_exp2(m[h] - mx);
+    float lh = l[h] * wgt;
+#pragma unroll
+    for (int sh = CPT; sh < 64; sh <<= 1) lh += shfl_xor(lh, sh);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v = o[h][j] * wgt;
+#pragma unroll
+      for (int sh = CPT; sh < 64; sh <<= 1) v += shfl_xor(v, sh);
+      o[h][j] = v;
+    }
+    m[h] = mx;
+    l[h] = lh;
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm_o[wave][h][8 * c + j] = o[h][j];
+      if (c == 0) {
+        sm_m[wave][h] = m[h];
+        sm_l[wave][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the waves and write ------------------------------------------
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+    const int h = e / D;
+    const int dd = e - h * D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    float lsum = 0.f, osum = 0.f;
+    if (mx != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w][h];
+        const float wt = (mw == kNegInf) ? 0.f : fast_exp2(mw - mx);
+        lsum = fmaf(wt, sm_l[w][h], lsum);
+        osum = fmaf(wt, sm_o[w][h][dd], osum);
+      }
+    }
+    if constexpr (MODE == kModeNoSplit) {
+      const int64_t qh = int64_t(row) * a.num_q_heads + g * G + h;
+      const float val = (lsum > 0.f) ? osum / lsum : 0.f;
+      static_cast<uint16_t*>(a.out)[qh * D + dd] = Elem<BF16>::from_float(val);
+      if (dd == 0 && a.lse) a.lse[qh] = (lsum > 0.f) ? mx * kLn2 + __logf(lsum) : kNegInf;
+    } else {
+      a.st_o[(slot * G + h) * D + dd] = osum;
+      if (dd == 0) {
+        a.st_m[slot * G + h] = (mx == kNegInf) ? kNegInf : mx * kLn2;
+        a.st_l[slot * G + h] = lsum;
+      }
+    }
+  }
+}
+
+template <int D, int GP, bool BF16, int NW>
+pkv_status launch_valu_modes(int mode, const SplitArgs& a, int grid, hipStream_t s) {
+  const dim3 block(NW * 64);
+  if (mode == kModeWorkqueue)
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, kModeWorkqueue>), dim3(grid), block, 0,
+                       s, a);
+  else if (mode == kModeBucket)
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, kModeBucket>), dim3(grid), block, 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, kModeNoSplit>), dim3(grid), block, 0,
+                       s, a);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+template <int D, bool BF16>
+pkv_status launch_valu_g(int gp, int mode, const SplitArgs& a, int grid, hipStream_t s) {
+  switch (gp) {
+    case 1: return launch_valu_modes<D, 1, BF16, 8>(mode, a, grid, s);
+    case 2: return launch_valu_modes<D, 2, BF16, 8>(mode, a, grid, s);
+    case 4: return launch_valu_modes<D, 4, BF16, 8>(mode, a, grid, s);
+    case 8: return launch_valu_modes<D, 8, BF16, 4>(mode, a, grid, s);
+    default: return PKV_ESHAPE;
+  }
+}
+
+}  // namespace
+
+// Group sizes up to 8 run on the vector ALUs with the group padded to the next
+// power of two (padded heads get q = 0 and are never written).
+pkv_status launch_split_valu(const pkv_problem& p, int mode, const SplitArgs& a, int grid,
+                             hipStream_t s) {
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 0;
+  if (gp == 0) return PKV_ESHAPE;
+  const bool bf = p.dtype == PKV_BF16;
+  if (p.head_dim == 128)
+    return bf ? launch_valu_g<128, true>(gp, mode, a, grid, s)
+              : launch_valu_g<128, false>(gp, mode, a, grid, s);
+  return bf ? launch_valu_g<64, true>(gp, mode, a, grid, s)
+            : launch_valu_g<64, false>(gp, mode, a, grid, s);
+}
+
+}  // namespace pkv

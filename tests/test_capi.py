@@ -1,0 +1,205 @@
+"""C-ABI tests that need no GPU: exports, host planner vs the planner oracle,
+policy vs the policy oracle, and argument validation (nothing is launched)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.planner import plan as oracle_plan
+from oracle.policy import choose as oracle_choose
+from paged_kv_gqa_block_amd import _lib
+from paged_kv_gqa_block_amd._lib import (PKV_BUCKETED, PKV_EDTYPE, PKV_EINVAL, PKV_ENOSPC,
+                                         PKV_ERANGE, PKV_ESHAPE, PKV_NOSPLIT, PKV_WORKQUEUE,
+                                         PATH_NAMES, PkvError)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "pkv.h")
+
+
+def test_library_exports_every_declared_symbol():
+    with open(HEADER) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(pkv_\w+)\s*\(", text, flags=re.M))
+    assert {"pkv_plan", "pkv_decode", "pkv_merge", "pkv_policy"} <= declared
+    for name in sorted(declared):
+        assert hasattr(_lib.LIB, name), name
+    assert set(_lib.EXPORTED) == declared
+
+
+def _prob(b, hq=32, hkv=8, d=128, max_pages=2048, dtype="f16", pool=4096):
+    return _lib.make_problem(b, hq, hkv, d, 16, pool, max_pages, dtype)
+
+
+def _plan(prob, lens, path, s):
+    nbytes = _lib.pkv_plan_bytes(prob, path, s)
+    buf = np.zeros(nbytes // 4, dtype=np.int32)
+    info = _lib.pkv_plan(prob, np.asarray(lens, dtype=np.int32), path, s, buf)
+    return info, _lib.decode_plan(buf)
+
+
+@pytest.mark.parametrize("seed", range(25))
+@pytest.mark.parametrize("path", [PKV_WORKQUEUE, PKV_BUCKETED, PKV_NOSPLIT])
+def test_host_planner_matches_oracle_bit_exactly(seed, path):
+    rng = np.random.default_rng(1000 + seed)
+    b = int(rng.integers(1, 17))
+    hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 4, 8]))
+    s = int(rng.choice([1, 2, 4, 7, 32, 64]))
+    kind = seed % 3
+    if kind == 0:
+        lens = rng.integers(0, 32768, size=b, endpoint=True)
+    elif kind == 1:  # many repeated lengths -> few buckets
+        lens = rng.choice([0, 1, 16, 17, 4096, 32768], size=b)
+    else:
+        lens = np.concatenate([rng.integers(128, 2048, b // 2, endpoint=True),
+                               rng.integers(16384, 32768, b - b // 2, endpoint=True)])
+    prob = _prob(b, hq=hkv * g, hkv=hkv)
+    info, got = _plan(prob, lens, path, s)
+    ref = oracle_plan(lens, hkv, hkv * g, 128, 16, s, PATH_NAMES[path])
+    assert got["tasks"] == ref.tasks
+    assert got["row_pages"] == ref.row_pages
+    assert got["row_nsplit"] == ref.row_nsplit
+    assert got["row_len"] == [int(x) for x in lens]
+    if path == PKV_WORKQUEUE:
+        assert got["row_task_off"] == ref.row_task_off
+        assert got["pages_per_split"] == ref.pages_per_split
+    if path == PKV_BUCKETED:
+        assert [(bk[0], bk[1], bk[2], bk[3], bk[4]) for bk in got["buckets"]] == [
+            (r[0], r[1], r[2], r[3], len(r[4])) for r in ref.buckets]
+        rows = []
+        for r in ref.buckets:
+            rows.extend(r[4])
+        assert got["bucket_rows"] == rows
+    assert info.n_tasks == len(ref.tasks)
+    assert info.n_launches == ref.n_launches
+    assert info.n_state_slots == ref.n_state_slots
+    assert info.n_empty_slots == ref.n_empty_slots
+    assert info.kv_bytes == ref.kv_bytes
+    assert info.merge_state_bytes == ref.merge_state_bytes
+    assert info.n_buckets == len(ref.buckets)
+    assert info.plan_bytes == got["total_words"] * 4
+    again = _lib.pkv_plan_get_info(prob, _plan_buf(prob, lens, path, s))
+    assert again.as_dict() == info.as_dict()
+
+
+def _plan_buf(prob, lens, path, s):
+    buf = np.zeros(_lib.pkv_plan_bytes(prob, path, s) // 4, dtype=np.int32)
+    _lib.pkv_plan(prob, np.asarray(lens, dtype=np.int32), path, s, buf)
+    return buf
+
+
+def test_fanout_16_to_2_through_the_c_planner():
+    rng = np.random.default_rng(20260623)
+    lens = np.concatenate([rng.integers(128, 2048, 4, endpoint=True),
+                           rng.integers(16384, 32768, 4, endpoint=True)])
+    prob = _prob(8)
+    assert _plan(prob, lens, PKV_BUCKETED, 32)[0].n_launches == 16
+    assert _plan(prob, lens, PKV_WORKQUEUE, 32)[0].n_launches == 2
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_policy_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    rules = []
+    for _ in range(int(rng.integers(1, 8))):
+        b_lo = int(rng.integers(1, 40))
+        n_lo = int(rng.integers(0, 20000))
+        rules.append((b_lo, b_lo + int(rng.integers(0, 40)), n_lo, n_lo + int(rng.integers(0, 20000)),
+                      int(rng.integers(0, 3)), int(rng.integers(1, 65))))
+    for _ in range(200):
+        b, n = int(rng.integers(1, 80)), int(rng.integers(0, 40000))
+        ref = oracle_choose(rules, b, n)
+        if ref is None:
+            with pytest.raises(PkvError) as e:
+                _lib.pkv_policy(rules, b, n)
+            assert e.value.status == PKV_ERANGE
+        else:
+            assert _lib.pkv_policy(rules, b, n) == ref
+
+
+def test_policy_errors():
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_policy([(1, 1, 0, 10, 7, 1)], 1, 1)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_policy([(1, 1, 0, 10, 1, 0)], 1, 1)
+    assert e.value.status == PKV_EINVAL
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_q_heads", 30, PKV_ESHAPE),   # Hq % Hkv != 0
+    ("num_q_heads", 8 * 17, PKV_ESHAPE),  # G = 17 > 16
+    ("head_dim", 96, PKV_ESHAPE),
+    ("page_size", 8, PKV_ESHAPE),
+    ("dtype", 7, PKV_EDTYPE),
+    ("batch", 0, PKV_EINVAL),
+    ("kernel", 9, PKV_EINVAL),
+    ("num_pool_pages", 0, PKV_EINVAL),
+])
+def test_plan_rejects_bad_problems(field, value, status):
+    prob = _prob(2)
+    setattr(prob, field, value)
+    buf = np.zeros(1 << 16, dtype=np.int32)
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_plan(prob, np.array([5, 6], np.int32), PKV_WORKQUEUE, 4, buf)
+    assert e.value.status == status
+    assert _lib.pkv_plan_bytes(prob, PKV_WORKQUEUE, 4) == 0
+
+
+def test_plan_rejects_bad_lengths_splits_and_small_buffers():
+    prob = _prob(2, max_pages=4)
+    buf = np.zeros(1 << 12, dtype=np.int32)
+    for lens in ([65, 1], [-1, 3]):
+        with pytest.raises(PkvError) as e:
+            _lib.pkv_plan(prob, np.array(lens, np.int32), PKV_WORKQUEUE, 4, buf)
+        assert e.value.status == PKV_ERANGE
+    _lib.pkv_plan(prob, np.array([64, 0], np.int32), PKV_WORKQUEUE, 4, buf)  # at capacity
+    for s in (0, 70000):
+        with pytest.raises(PkvError) as e:
+            _lib.pkv_plan(prob, np.array([5, 1], np.int32), PKV_WORKQUEUE, s, buf)
+        assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_plan(prob, np.array([5, 1], np.int32), 3, 4, buf)
+    assert e.value.status == PKV_EINVAL
+    need = _lib.pkv_plan_bytes(prob, PKV_WORKQUEUE, 4)
+    small = np.zeros(need // 4 - 1, dtype=np.int32)
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_plan(prob, np.array([5, 1], np.int32), PKV_WORKQUEUE, 4, small,
+                      plan_bytes=small.nbytes)
+    assert e.value.status == PKV_ENOSPC
+
+
+def test_decode_and_merge_validate_before_launch():
+    prob = _prob(2)
+    buf = _plan_buf(prob, [40, 3], PKV_WORKQUEUE, 4)
+    other = _prob(3)
+    fake = 0x1000  # never dereferenced: every call below fails validation first
+    with pytest.raises(PkvError) as e:  # plan made for another batch size
+        _lib.pkv_decode(other, buf, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ESHAPE
+    with pytest.raises(PkvError) as e:  # missing q
+        _lib.pkv_decode(prob, buf, fake, None, fake, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:  # missing states on a split path
+        _lib.pkv_decode(prob, buf, fake, fake, fake, fake, fake, fake, None, None, None)
+    assert e.value.status == PKV_EINVAL
+    bad = buf.copy()
+    bad[0] = 0
+    with pytest.raises(PkvError) as e:  # not a plan
+        _lib.pkv_merge(prob, bad, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:  # missing output
+        _lib.pkv_merge(prob, buf, fake, fake, fake, fake, None)
+    assert e.value.status == PKV_EINVAL
+    bad_dt = _prob(2, dtype="f16")
+    bad_dt.dtype = 5
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_merge(bad_dt, buf, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_EDTYPE
+
+
+def test_status_strings():
+    for s in range(-6, 1):
+        assert _lib.pkv_status_str(s)
+    assert _lib.pkv_status_str(-99) == "unknown status"

@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every input is seeded and synthetic; pools hold NaN in every unused page and
+in every slot past a row's last real token, so any read of padding shows up
+as a non-finite or wrong output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_gqa_block_amd import engine, traces
+from paged_kv_gqa_block_amd._lib import PKV_PLAN_HEADER_WORDS  # noqa: F401
+from tests.parity import check_lse, check_out, oracle_out, say
+
+pytestmark = pytest.mark.gpu
+
+SEED = traces.HELD_OUT_SEED
+PATHS = ("bucketed", "workqueue", "nosplit")
+KERNELS = ("valu",)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    torch.cuda.init()
+
+
+def _run(w, path, splits, kernel):
+    wd = engine.to_device(w)
+    engine.validate_inputs(wd)
+    prob = engine.problem_from_workload(w, kernel)
+    step = engine.DecodeStep(prob, path, splits)
+    step.plan(wd["seq_lens_host"])
+    step.run(wd)
+    torch.cuda.synchronize()
+    return step, wd
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_config_all_paths(path, kernel):
+    w = traces.generate(traces.get_spec("tiny"), SEED)
+    say(f"[tiny] path={path} kernel={kernel}")
+    ref_out, ref_lse = oracle_out(w)
+    step, _ = _run(w, path, w["spec"].splits, kernel)
+    check_out(step.out, ref_out, "f16", label=f"tiny/{path}")
+    check_lse(step.lse, ref_lse, label=f"tiny/{path}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("path", ("workqueue", "bucketed"))
+def test_split_states_match_oracle(path, kernel):
+    spec = traces.custom_spec(3, 8, 2, 64, splits=5)
+    lens = np.array([200, 37, 0], dtype=np.int32)
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    say(f"[states] path={path} kernel={kernel}")
+    step, _ = _run(w, path, 5, kernel)
+    a = traces.oracle_arrays(w)
+    plan = oracle.plan(lens, 2, 8, 64, 16, 5, path)
+    m, l, o = oracle.split_states_for_plan(a["q"], a["k_pool"], a["v_pool"], a["block_table"],
+                                           plan.tasks, a["scale"], 16, "f16", 4, lens)
+    gm = step.st_m.cpu().numpy().astype(np.float64)
+    gl = step.st_l.cpu().numpy().astype(np.float64)
+    go = step.st_o.cpu().numpy().astype(np.float64)
+    for j, (row, g, s, _pb, _pe) in enumerate(plan.tasks):
+        slot = j if path == "workqueue" else (row * 2 + g) * 5 + s
+        lse_ref = m[j] + np.log(l[j])
+        lse_got = gm[slot] + np.log(gl[slot])
+        assert np.abs(lse_got - lse_ref).max() <= 2e-4, (j, lse_got, lse_ref)
+        on_ref = o[j] / l[j][:, None]
+        on_got = go[slot] / gl[slot][:, None]
+        assert np.abs(on_got - on_ref).max() <= 1e-4, j
+    if path == "bucketed":
+        used = {(row * 2 + g) * 5 + s for (row, g, s, _, _) in plan.tasks}
+        for slot in range(plan.n_state_slots):
+            if slot not in used:
+                assert np.isneginf(gm[slot]).all() and (gl[slot] == 0).all()
+                assert (go[slot] == 0).all()
+
+
+def test_merge_kernel_from_oracle_states():
+    """The merge alone, fed with oracle states (fp64 rounded to fp32)."""
+    spec = traces.custom_spec(4, 16, 2, 128, splits=7)
+    lens = np.array([1000, 3, 0, 517], dtype=np.int32)
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    say("[merge-only]")
+    a = traces.oracle_arrays(w)
+    plan = oracle.plan(lens, 2, 16, 128, 16, 7, "workqueue")
+    m, l, o = oracle.split_states_for_plan(a["q"], a["k_pool"], a["v_pool"], a["block_table"],
+                                           plan.tasks, a["scale"], 16, "f16", 8, lens)
+    wd = engine.to_device(w)
+    prob = engine.problem_from_workload(w, "valu")
+    step = engine.DecodeStep(prob, "workqueue", 7)
+    step.plan(wd["seq_lens_host"])
+    n = len(plan.tasks)
+    step.st_m[:n] = torch.from_numpy(m.astype(np.float32)).cuda()
+    step.st_l[:n] = torch.from_numpy(l.astype(np.float32)).cuda()
+    step.st_o[:n] = torch.from_numpy(o.astype(np.float32)).cuda()
+    step.merge()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_out(w)
+    check_out(step.out, ref_out, "f16", label="merge-only")
+    check_lse(step.lse, ref_lse, label="merge-only")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("name,paths", [
+    ("long", ("bucketed", "workqueue", "nosplit")),
+    ("bimodal", ("workqueue", "bucketed", "nosplit")),
+    ("zipf", ("workqueue", "bucketed", "nosplit")),
+    ("uniform", ("workqueue",)),
+])
+def test_full_size_configs(name, paths, kernel):
+    w = traces.generate(traces.get_spec(name), SEED)
+    say(f"[{name}] lens={w['seq_lens'].tolist()} kernel={kernel}")
+    ref_out, ref_lse = oracle_out(w)
+    for path in paths:
+        say(f"  path={path}")
+        step, _ = _run(w, path, w["spec"].splits, kernel)
+        mx, rel = check_out(step.out, ref_out, "f16", label=f"{name}/{path}")
+        check_lse(step.lse, ref_lse, label=f"{name}/{path}")
+        say(f"  ok max-abs={mx:.2e} rel-l2={rel:.2e}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("batch", (1, 8))
+def test_policy_sweep_slice_bf16(batch, kernel):
+    w = traces.generate(traces.get_spec(f"policy_b{batch}"), SEED)
+    say(f"[policy_b{batch}] kernel={kernel}")
+    ref_out, ref_lse = oracle_out(w)
+    for path, s in (("workqueue", 32), ("bucketed", 16), ("nosplit", 1)):
+        step, _ = _run(w, path, s, kernel)
+        check_out(step.out, ref_out, "bf16", label=f"policy_b{batch}/{path}")
+        check_lse(step.lse, ref_lse, label=f"policy_b{batch}/{path}")
+
+
+EDGE_LENS = np.array([0, 1, 15, 16, 17, 33, 100, 0, 250], dtype=np.int32)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("d", (64, 128))
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (6, 2), (12, 2)])
+@pytest.mark.parametrize("dtype", ("f16", "bf16"))
+def test_edge_lengths_shapes_and_dtypes(d, hq, hkv, dtype, kernel):
+    spec = traces.custom_spec(len(EDGE_LENS), hq, hkv, d, splits=3, dtype=dtype)
+    w = traces.generate(spec, SEED, seq_lens=EDGE_LENS)
+    say(f"[edge] d={d} hq={hq} hkv={hkv} {dtype} kernel={kernel}")
+    ref_out, ref_lse = oracle_out(w)
+    for path, s in (("workqueue", 3), ("workqueue", 40), ("bucketed", 3), ("bucketed", 40),
+                    ("nosplit", 1)):
+        step, _ = _run(w, path, s, kernel)
+        check_out(step.out, ref_out, dtype, label=f"edge/{path}/S={s}")
+        check_lse(step.lse, ref_lse, label=f"edge/{path}/S={s}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("path", PATHS)
+def test_all_rows_empty(path, kernel):
+    spec = traces.custom_spec(3, 8, 2, 128, splits=4)
+    w = traces.generate(spec, SEED, seq_lens=np.zeros(3, np.int32))
+    say(f"[empty] path={path}")
+    step, _ = _run(w, path, 4, kernel)
+    assert (step.out.float() == 0).all()
+    assert torch.isneginf(step.lse).all()
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("dtype", ("f16", "bf16"))
+def test_single_token_gives_v_bit_exactly(dtype, kernel):
+    spec = traces.custom_spec(2, 8, 2, 128, splits=4, dtype=dtype)
+    w = traces.generate(spec, SEED, seq_lens=np.array([1, 1], np.int32))
+    say(f"[n=1] {dtype}")
+    for path in PATHS:
+        step, _ = _run(w, path, 4, kernel)
+        bt = w["block_table"]
+        for i in range(2):
+            for h in range(8):
+                v = w["v_pool"][bt[i, 0], h // 4, 0]
+                assert torch.equal(step.out[i, h].cpu().view(torch.int16), v.view(torch.int16))
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_two_runs_are_bit_identical(kernel):
+    w = traces.generate(traces.get_spec("bimodal"), SEED)
+    say("[determinism]")
+    s1, wd = _run(w, "workqueue", 32, kernel)
+    o1 = s1.out.clone()
+    s1.run(wd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), s1.out.view(torch.int16))
