@@ -101,9 +101,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// 16-byte global load that bypasses nothing special; kept as one dwordx4.
+// Plain 16-byte global load (one dwordx4).
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *static_cast<const uint4*>(p);
+}
+
+// Word 3 of a raw buffer descriptor on gfx9 (32-bit data format, no
+// swizzle): offsets at or past num_records read as zero without a memory
+// access.
+constexpr int kBufferFlags = 0x00020000;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 }  // namespace pkv

@@ -8,34 +8,26 @@
 // out = sum w_s o_s / L, lse = M + ln L.  Neutral states (m = -inf) weigh 0;
 // a row with only neutral states gets out = 0 and lse = -inf.
 //
-// One wave per (row, query head); 4 waves per workgroup.  Lane s first owns
-// split s (weights and the sum L via wave reductions), then lanes own output
-// elements and accumulate the weighted o_s, loading the per-split weight
-// through a wave broadcast.
+// One 256-thread workgroup per (row, query head).  Thread t owns output
+// chunk t % (d/4) (four floats) and split group t / (d/4); the split groups
+// walk the row's states with a stride, so every state load of the row is
+// issued up front.  Each thread keeps an online-rescaled partial (max, sum,
+// 4 outputs); split groups are then combined through LDS.
 #include "device_common.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) x = fmaxf(x, shfl_xor(x, sh));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) x += shfl_xor(x, sh);
-  return x;
-}
-
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int EPL = D / 64;  // output elements per lane
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);  // (row index, q head)
-  if (item >= a.num_rows * a.num_q_heads) return;
+  constexpr int CH = D / 4;    // float4 chunks per output row
+  constexpr int SG = 256 / CH; // split groups
+  constexpr int U = 4;         // states loaded per thread per round
+  const int t = threadIdx.x;
+  const int ch = t % CH;
+  const int sg = t / CH;
+  const int item = blockIdx.x;  // (row index, q head)
   const int ri = item / a.num_q_heads;
   const int h = item - ri * a.num_q_heads;
   const int hkv = a.num_kv_heads;
@@ -54,44 +46,77 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     base = (int64_t(row) * hkv + g) * a.splits;
   }
 
-  // Pass 1: global max over the splits.
-  float mx = kNegInf;
-  for (int s0 = 0; s0 < nsplit; s0 += 64) {
-    const int s = s0 + lane;
-    if (s < nsplit) mx = fmaxf(mx, a.st_m[(base + s) * G + hh]);
-  }
-  mx = wave_max(mx);
+  __shared__ float s_m[SG], s_l[SG];
+  __shared__ float4 s_o[SG][CH];
 
-  float acc[EPL];
+  float mloc = kNegInf, lloc = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = sg; s0 < nsplit; s0 += SG * U) {
+    float ms[U], ls[U];
+    float4 os[U];
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  float lsum = 0.f;
-  if (mx != kNegInf) {
-    for (int s0 = 0; s0 < nsplit; s0 += 64) {
-      const int s = s0 + lane;
-      float w = 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * SG;
       if (s < nsplit) {
-        const float ms = a.st_m[(base + s) * G + hh];
-        w = (ms == kNegInf) ? 0.f : __expf(ms - mx);
-        lsum = fmaf(w, a.st_l[(base + s) * G + hh], lsum);
-      }
-      const int cnt = min(64, nsplit - s0);
-      for (int k = 0; k < cnt; ++k) {
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
-        if (wk == 0.f) continue;  // wave-uniform skip of neutral / negligible states
-        const float* op = a.st_o + ((base + s0 + k) * G + hh) * D + lane * EPL;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) acc[j] = fmaf(wk, op[j], acc[j]);
+        const int64_t e = (base + s) * G + hh;
+        ms[u] = a.st_m[e];
+        ls[u] = a.st_l[e];
+        os[u] = reinterpret_cast<const float4*>(a.st_o + e * D)[ch];
+      } else {
+        ms[u] = kNegInf;
+        ls[u] = 0.f;
+        os[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
-    lsum = wave_sum(lsum);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ms[u] == kNegInf) continue;  // neutral state
+      const float mn = fmaxf(mloc, ms[u]);
+      const float a1 = (mloc == kNegInf) ? 0.f : __expf(mloc - mn);
+      const float a2 = __expf(ms[u] - mn);
+      lloc = lloc * a1 + ls[u] * a2;
+      acc.x = acc.x * a1 + os[u].x * a2;
+      acc.y = acc.y * a1 + os[u].y * a2;
+      acc.z = acc.z * a1 + os[u].z * a2;
+      acc.w = acc.w * a1 + os[u].w * a2;
+      mloc = mn;
+    }
+  }
+  if (ch == 0) {
+    s_m[sg] = mloc;
+    s_l[sg] = lloc;
+  }
+  s_o[sg][ch] = acc;
+  __syncthreads();
+  if (t >= CH) return;
+
+  float mx = kNegInf;
+#pragma unroll
+  for (int k = 0; k < SG; ++k) mx = fmaxf(mx, s_m[k]);
+  float lsum = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (mx != kNegInf) {
+#pragma unroll
+    for (int k = 0; k < SG; ++k) {
+      const float mk = s_m[k];
+      const float wk = (mk == kNegInf) ? 0.f : __expf(mk - mx);
+      lsum = fmaf(wk, s_l[k], lsum);
+      const float4 v = s_o[k][t];
+      o.x = fmaf(wk, v.x, o.x);
+      o.y = fmaf(wk, v.y, o.y);
+      o.z = fmaf(wk, v.z, o.z);
+      o.w = fmaf(wk, v.w, o.w);
+    }
   }
   const int64_t qh = int64_t(row) * a.num_q_heads + h;
-  uint16_t* out = static_cast<uint16_t*>(a.out) + qh * D + lane * EPL;
   const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) out[j] = Elem<BF16>::from_float(acc[j] * inv);
-  if (a.lse && lane == 0) a.lse[qh] = (lsum > 0.f) ? mx + __logf(lsum) : kNegInf;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + qh * D + 4 * t;
+  const uint32_t lo = Elem<BF16>::from_float(o.x * inv) |
+                      (uint32_t(Elem<BF16>::from_float(o.y * inv)) << 16);
+  const uint32_t hi = Elem<BF16>::from_float(o.z * inv) |
+                      (uint32_t(Elem<BF16>::from_float(o.w * inv)) << 16);
+  *reinterpret_cast<uint2*>(out) = make_uint2(lo, hi);
+  if (a.lse && t == 0) a.lse[qh] = (lsum > 0.f) ? mx + __logf(lsum) : kNegInf;
 }
 
 }  // namespace
@@ -99,7 +124,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 pkv_status launch_merge(const pkv_problem& p, const MergeArgs& a, hipStream_t s) {
   const int items = a.num_rows * p.num_q_heads;
   if (items == 0) return PKV_OK;
-  const dim3 grid((items + 3) / 4), block(256);
+  const dim3 grid(items), block(256);
   const bool bf = p.dtype == PKV_BF16;
   if (p.head_dim == 128) {
     if (bf) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, s, a);
@@ -111,15 +136,17 @@ pkv_status launch_merge(const pkv_problem& p, const MergeArgs& a, hipStream_t s)
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-// Chooses the split-kernel arithmetic.  AUTO currently means the vector-ALU
-// kernel; the matrix-core kernel is selected explicitly.
 pkv_status launch_split_valu(const pkv_problem& p, int mode, const SplitArgs& a, int grid,
                              hipStream_t s);
+pkv_status launch_split_mfma(const pkv_problem& p, int mode, const SplitArgs& a, int grid,
+                             hipStream_t s);
 
+// Chooses the split-kernel arithmetic.  AUTO currently means the vector-ALU
+// kernel; the matrix-core kernel (d = 128) is selected explicitly.
 pkv_status launch_split(const pkv_problem& p, int mode, int kernel, const SplitArgs& a, int grid,
                         hipStream_t s) {
   if (grid <= 0) return PKV_OK;
-  if (kernel == PKV_KERNEL_MFMA) return PKV_ESHAPE;
+  if (kernel == PKV_KERNEL_MFMA) return launch_split_mfma(p, mode, a, grid, s);
   return launch_split_valu(p, mode, a, grid, s);
 }
 

@@ -1,0 +1,409 @@
+// Split / no-split decode kernel, matrix-core variant (gfx950, d = 128).
+//
+// Same task decomposition, page ring and buffer-descriptor loads as the
+// vector-ALU kernel (split_valu.hip); the difference is the P*V product.
+//
+// Lane layout after one page is loaded (coalesced 16-byte loads): lane l holds
+// tokens kg, kg+4, kg+8, kg+12 of the page (kg = l / 16) and elements
+// [8c, 8c+8) of each (c = l % 16).
+//
+//  * Scores run on v_mfma_f32_16x16x32: A = K [16 tokens x 32 elements],
+//    B = Q^T [32 elements x 16 heads (padded)], D = S [16 tokens x 16 heads].
+//    MFMA operands want one token per lane column, the transpose of the
+//    coalesced layout, so each wave writes its K page into a private LDS tile
+//    (ds_write_b128, rows XOR-swizzled so neither the writes nor the MFMA
+//    reads conflict on banks) and reads it back in operand order.  A's row m
+//    is token (m / 4) + 4 (m % 4): then the D registers of lane (kg, c) are the
+//    scores of head c for tokens kg + 4r -- the lane's own tokens.
+//  * Softmax uses one running max per query head for the whole wave: lane
+//    (kg, c) owns head c and reduces the page max over the 4 row groups with
+//    cross-row lane swaps.
+//  * P*V runs on v_mfma_f32_16x16x16: A = P [16 heads x 16 tokens],
+//    B = V [16 tokens x 16 output elements], D = O [16 heads x 16 elements].
+//    Token slot k = 4*kg + i is token kg + 4i, which is what lane (n, kg)
+//    holds in V load i, so B needs only byte permutes: MFMA j (0..7) covers
+//    output elements 8n + j.  A is the lane's own p values for head c, split
+//    into a 16-bit high part and a 16-bit residual so the product keeps
+//    fp32-level precision in P.
+//  * O is rescaled only when some head's running max grew (wave-uniform
+//    test), which after the first pages is rare.
+//
+// Method: PersistentKV summary pages, "Methodology / 1. Native block-table
+// decode engine" (GQA over paged KV read through the block table, partial
+// online-softmax state per disjoint split, empty splits write neutral state).
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// 16 x 16 x 32 score product (A = K rows, B = Q^T columns).
+template <bool BF16>
+__device__ __forceinline__ float4_t mfma_qk(const uint4& a, const uint4& b, float4_t c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+// Physical 16-byte chunk of (token t, chunk ch) inside a 256-byte K-tile row.
+// The XOR key maps the 16 tokens the MFMA reads together onto 16 distinct
+// chunk positions.
+__device__ __forceinline__ int ktile_chunk(int t, int ch) {
+  return ch ^ (((t & 3) << 2) | (t >> 2));
+}
+
+// Cross-row reductions with the gfx950 row-swap instructions.  With both
+// operands equal to x, the two results of a swap hold, in every lane l, the
+// values of lanes l and l ^ 16 (permlane16) or l and l ^ 32 (permlane32), in
+// some order; combining them with a symmetric op reduces across the rows.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// P operands.  P is split into a 16-bit high part and the 16-bit rounding of
+// its residual, P ~= hi + lo with about 22 (fp16) or 16 (bf16) significant
+// bits; both parts go through the matrix core, so the product keeps
+// fp32-level precision in P.
+template <bool BF16>
+struct Pv;
+
+template <>
+struct Pv<false> {  // fp16 P and V
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const half2_t h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return Elem<false>::lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return Elem<false>::hi(w); }
+  static __device__ __forceinline__ float4_t mfma(uint2 a, uint2 b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                                 __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Pv<true> {  // bf16 P and V
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return uint32_t(Elem<true>::from_float(a)) | (uint32_t(Elem<true>::from_float(b)) << 16);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return Elem<true>::lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return Elem<true>::hi(w); }
+  static __device__ __forceinline__ float4_t mfma(uint2 a, uint2 b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a),
+                                                     __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
+  }
+};
+
+template <int GP, bool BF16, int NW, int PF, int MODE>
+__global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
+  constexpr int D = 128;
+  constexpr int NL = 4;      // 16-byte loads per page per pool (4 tokens each)
+  constexpr int HR = (GP + 3) / 4;  // MFMA output row groups holding real heads
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15;   // element chunk [8c, 8c+8); also MFMA column n / head m
+  const int kg = lane >> 4;  // row group: tokens kg + 4i
+  const int hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / hkv;
+
+  __shared__ float sm_m[NW][GP];
+  __shared__ float sm_l[NW][GP];
+  __shared__ float sm_o[NW][GP][D];
+  __shared__ uint4 sm_k[NW][16][16];  // per-wave K tile: [token][physical chunk]
+
+  // ---- task (identical to the vector-ALU kernel) ---------------------------
+  const int item = blockIdx.x;
+  int row, g, pb, pe;
+  int64_t slot = 0;
+  if constexpr (MODE == kModeWorkqueue) {
+    const int4 t = reinterpret_cast<const int4*>(a.tasks)[item];
+    row = t.x;
+    g = t.y >> 16;
+    pb = t.z;
+    pe = t.w;
+    slot = item;
+  } else if constexpr (MODE == kModeBucket) {
+    const int s = item % a.splits;
+    const int rest = item / a.splits;
+    g = rest % hkv;
+    row = a.bucket_rows[rest / hkv];
+    slot = (int64_t(row) * hkv + g) * a.splits + s;
+    if (s >= a.bucket_nsplit) {  // empty split: neutral state, exit early
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) a.st_o[slot * G * D + e] = 0.f;
+      if (threadIdx.x < G) {
+        a.st_m[slot * G + threadIdx.x] = kNegInf;
+        a.st_l[slot * G + threadIdx.x] = 0.f;
+      }
+      return;
+    }
+    pb = s * a.bucket_pps;
+    pe = min(pb + a.bucket_pps, a.bucket_pages);
+  } else {
+    row = item / hkv;
+    g = item % hkv;
+    pb = 0;
+    pe = 0;
+  }
+  const int n = a.seq_lens[row];
+  if constexpr (MODE == kModeNoSplit) {
+    pe = (n + 15) >> 4;
+    if (pe == 0) {
+      uint16_t* out = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.num_q_heads + g * G) * D;
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) out[e] = 0;
+      if (a.lse && threadIdx.x < G) a.lse[int64_t(row) * a.num_q_heads + g * G + threadIdx.x] =
+          kNegInf;
+      return;
+    }
+  }
+
+  // B operand of the score MFMAs: lane (kg, c) holds elements
+  // [32t + 8kg, 32t + 8kg + 8) of head c for MFMA t (zero for padded heads).
+  uint4 qb[4];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (int64_t(row) * a.num_q_heads + g * G + c) * D + 8 * kg;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qb[t] = (c < G) ? load16(qp + 32 * t) : zero4();
+  }
+  // Token read by this lane as MFMA A row m = c.
+  const int a_tok = (c >> 2) + 4 * (c & 3);
+
+  // Running max of head c (this lane's softmax head) in log2 units, this
+  // lane's share of the sum, and the MFMA accumulators O[j][r]:
+  // O[4*kg + r][8*c + j].
+  float m_run = kNegInf, l_part = 0.f;
+  float4_t acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t page_stride = int64_t(hkv) * 16 * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + int64_t(g) * 16 * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + int64_t(g) * 16 * D;
+  const int32_t* bt = a.block_table + int64_t(row) * a.max_pages;
+  const float sl2 = a.scale_log2;
+  const int first = pb + wave;
+  const int cnt = (pe > first) ? (pe - first + NW - 1) / NW : 0;
+
+  int kc = 0;
+  int pids = 0;
+  auto page_rsrc = [&](const uint16_t* base, int j, int cnt_c) {
+    int nbytes = 0;
+    const uint16_t* ptr = base;
+    if (j < cnt_c) {
+      const int pid = __builtin_amdgcn_readlane(pids, j);
+      const int valid = min(16, n - (first + (kc + j) * NW) * 16);
+      nbytes = valid * D * 2;
+      ptr = base + int64_t(pid) * page_stride;
+    }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ptr), (short)0, nbytes,
+                                             kBufferFlags);
+  };
+  auto issue = [&](int j, int cnt_c, uint4 (&kk)[NL], uint4 (&vv)[NL]) {
+    const auto kr = page_rsrc(kbase, j, cnt_c);
+    const auto vr = page_rsrc(vbase, j, cnt_c);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      kk[i] = buffer_load16(kr, lane * 16 + i * 1024);
+      vv[i] = buffer_load16(vr, lane * 16 + i * 1024);
+    }
+  };
+
+  auto compute_page = [&](int j, const uint4 (&kk)[NL], const uint4 (&vv)[NL]) {
+    const int valid = n - (first + (kc + j) * NW) * 16;
+    // K page -> LDS tile (token kg + 4i, chunk c), then back in A order.
+    uint4 (&tile)[16][16] = sm_k[wave];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int t = kg + 4 * i;
+      tile[t][ktile_chunk(t, c)] = kk[i];
+    }
+    float4_t sacc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      sacc = mfma_qk<BF16>(tile[a_tok][ktile_chunk(a_tok, 4 * t + kg)], qb[t], sacc);
+    // Scores of head c for this lane's tokens kg + 4i, in log2 units.
+    float xs[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) xs[i] = sacc[i] * sl2;
+    if (valid < 16) {  // tail page: tokens kg + 4i >= valid do not exist
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if (kg + 4 * i >= valid) xs[i] = kNegInf;
+    }
+    float mp = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+    mp = max_xor32(max_xor16(mp));  // page max of head c over all 16 tokens
+    const float mn = fmaxf(m_run, mp);  // finite: every page has a real token
+    const bool grew = mn > m_run;
+    if (__builtin_amdgcn_ballot_w64(grew) != 0) {  // rescale O and l to the new max
+      const float alpha = fast_exp2(m_run - mn);
+      l_part *= alpha;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // O row 4*kg + r belongs to head 4*kg + r, whose alpha sits in lane
+        // (row 0, column 4*kg + r).
+        const float ar = __int_as_float(
+            __builtin_amdgcn_ds_bpermute((4 * kg + r) << 2, __float_as_int(alpha)));
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc[jj][r] *= ar;
+      }
+      m_run = mn;
+    }
+    float p[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      p[i] = fast_exp2(xs[i] - m_run);
+      l_part += p[i];
+    }
+    // B operands: element 8c + jj of tokens kg + 4i, i = 0..3.
+    const uint32_t w[NL][4] = {{vv[0].x, vv[0].y, vv[0].z, vv[0].w},
+                               {vv[1].x, vv[1].y, vv[1].z, vv[1].w},
+                               {vv[2].x, vv[2].y, vv[2].z, vv[2].w},
+                               {vv[3].x, vv[3].y, vv[3].z, vv[3].w}};
+    using PV = Pv<BF16>;
+    const uint2 ph = make_uint2(PV::pack2(p[0], p[1]), PV::pack2(p[2], p[3]));
+    const uint2 pl = make_uint2(PV::pack2(p[0] - PV::lo(ph.x), p[1] - PV::hi(ph.x)),
+                                PV::pack2(p[2] - PV::lo(ph.y), p[3] - PV::hi(ph.y)));
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+      const uint2 bv = make_uint2(__builtin_amdgcn_perm(w[1][jj >> 1], w[0][jj >> 1], sel),
+                                  __builtin_amdgcn_perm(w[3][jj >> 1], w[2][jj >> 1], sel));
+      acc[jj] = PV::mfma(ph, bv, acc[jj]);
+      acc[jj] = PV::mfma(pl, bv, acc[jj]);
+    }
+  };
+
+  constexpr int R = PF + 1;
+  uint4 kb[R][NL], vb[R][NL];
+  for (kc = 0; kc < cnt; kc += 64) {
+    const int cnt_c = min(64, cnt - kc);
+    pids = (lane < cnt_c) ? bt[first + (kc + lane) * NW] : 0;
+#pragma unroll
+    for (int u = 0; u < PF; ++u) issue(u, cnt_c, kb[u], vb[u]);
+    for (int j0 = 0; j0 < cnt_c; j0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int j = j0 + u;
+        issue(j + PF, cnt_c, kb[(u + PF) % R], vb[(u + PF) % R]);
+        if (j < cnt_c) compute_page(j, kb[u], vb[u]);
+      }
+    }
+  }
+
+  // ---- wave totals: l summed over the 4 row groups -------------------------
+  const float l_tot = sum_xor32(sum_xor16(l_part));
+  if (kg < HR) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * kg + r;
+      if (h < GP) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sm_o[wave][h][8 * c + jj] = acc[jj][r];
+      }
+    }
+  }
+  if (lane < GP) {
+    sm_m[wave][lane] = m_run;  // -inf when the wave had no pages
+    sm_l[wave][lane] = l_tot;
+  }
+  __syncthreads();
+
+  // ---- merge the waves and write (identical to the vector-ALU kernel) ------
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+    const int h = e / D;
+    const int dd = e - h * D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    float lsum = 0.f, osum = 0.f;
+    if (mx != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w][h];
+        const float wt = (mw == kNegInf) ? 0.f : fast_exp2(mw - mx);
+        lsum = fmaf(wt, sm_l[w][h], lsum);
+        osum = fmaf(wt, sm_o[w][h][dd], osum);
+      }
+    }
+    if constexpr (MODE == kModeNoSplit) {
+      const int64_t qh = int64_t(row) * a.num_q_heads + g * G + h;
+      const float val = (lsum > 0.f) ? osum / lsum : 0.f;
+      static_cast<uint16_t*>(a.out)[qh * D + dd] = Elem<BF16>::from_float(val);
+      if (dd == 0 && a.lse) a.lse[qh] = (lsum > 0.f) ? mx * kLn2 + __logf(lsum) : kNegInf;
+    } else {
+      a.st_o[(slot * G + h) * D + dd] = osum;
+      if (dd == 0) {
+        a.st_m[slot * G + h] = (mx == kNegInf) ? kNegInf : mx * kLn2;
+        a.st_l[slot * G + h] = lsum;
+      }
+    }
+  }
+}
+
+template <int GP, bool BF16, int NW, int PF>
+pkv_status launch_mfma_modes(int mode, const SplitArgs& a, int grid, hipStream_t s) {
+  const dim3 block(NW * 64);
+  if (mode == kModeWorkqueue)
+    hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeWorkqueue>), dim3(grid), block, 0,
+                       s, a);
+  else if (mode == kModeBucket)
+    hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeBucket>), dim3(grid), block, 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeNoSplit>), dim3(grid), block, 0,
+                       s, a);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+template <bool BF16>
+pkv_status launch_mfma_g(int gp, int mode, const SplitArgs& a, int grid, hipStream_t s) {
+  switch (gp) {
+    case 1: return launch_mfma_modes<1, BF16, 8, 2>(mode, a, grid, s);
+    case 2: return launch_mfma_modes<2, BF16, 8, 2>(mode, a, grid, s);
+    case 4: return launch_mfma_modes<4, BF16, 8, 2>(mode, a, grid, s);
+    case 8: return launch_mfma_modes<8, BF16, 8, 2>(mode, a, grid, s);
+    case 16: return launch_mfma_modes<16, BF16, 4, 2>(mode, a, grid, s);
+    default: return PKV_ESHAPE;
+  }
+}
+
+}  // namespace
+
+// d = 128 only; the group is padded to the next power of two (<= 16).
+pkv_status launch_split_mfma(const pkv_problem& p, int mode, const SplitArgs& a, int grid,
+                             hipStream_t s) {
+  if (p.head_dim != 128) return PKV_ESHAPE;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : G <= 16 ? 16 : 0;
+  if (gp == 0) return PKV_ESHAPE;
+  return p.dtype == PKV_BF16 ? launch_mfma_g<true>(gp, mode, a, grid, s)
+                             : launch_mfma_g<false>(gp, mode, a, grid, s);
+}
+
+}  // namespace pkv

@@ -2,9 +2,9 @@
 //
 // One workgroup per task (row, kv head, page range).  The pages of the task
 // are dealt round-robin to the workgroup's waves; a wave reads one whole KV
-// page per step with coalesced 16-byte loads (one wave-wide load covers
-// 1 KiB, i.e. 64/(d/8) tokens), and keeps the next page in flight while it
-// computes the current one.  Lane layout after a load: the d/8 lanes of a
+// page per step with coalesced 16-byte buffer loads (one wave-wide load
+// covers 1 KiB, i.e. 64/(d/8) tokens), and keeps PF more pages in flight
+// while it computes the current one.  Lane layout after a load: the d/8 lanes of a
 // "stream" hold one token row, 8 elements each; a wave holds 64/(d/8)
 // streams.  Scores are packed dot products (v_dot2) reduced across the
 // stream's lanes with DPP; every stream keeps its own running max / sum /
@@ -22,7 +22,7 @@
 namespace pkv {
 namespace {
 
-template <int D, int GP, bool BF16, int NW, int MODE>
+template <int D, int GP, bool BF16, int NW, int PF, int MODE>
 __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
   constexpr int CPT = D / 8;     // 16-byte chunks per token row
   constexpr int TPI = 64 / CPT;  // tokens per wave-wide 16-byte load
@@ -102,38 +102,47 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
   }
 
   const int64_t page_stride = int64_t(hkv) * 16 * D;  // elements
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + int64_t(g) * 16 * D + 8 * lane;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + int64_t(g) * 16 * D + 8 * lane;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + int64_t(g) * 16 * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + int64_t(g) * 16 * D;
   const int32_t* bt = a.block_table + int64_t(row) * a.max_pages;
   const float sl2 = a.scale_log2;
 
+  // This wave's pages: first, first + NW, ... (cnt of them).
   const int first = pb + wave;
   const int cnt = (pe > first) ? (pe - first + NW - 1) / NW : 0;
 
-  auto load_page = [&](int k, uint4 (&kk)[NL], uint4 (&vv)[NL]) {
-    const int pg = first + k * NW;
-    const int pid = bt[pg];
-    const uint16_t* kp = kbase + int64_t(pid) * page_stride;
-    const uint16_t* vp = vbase + int64_t(pid) * page_stride;
-    const int valid = n - pg * 16;  // real tokens in this page (>= 1)
-    if (valid >= 16) {
+  // Block-table entries of the current chunk of (up to) 64 of the wave's
+  // pages: lane j holds the pool page of the wave's page kc + j.
+  int kc = 0;
+  int pids = 0;
+
+  // Buffer descriptor of the chunk's page j: num_records = bytes of its real
+  // tokens, so loads of tokens past N -- and of null pages j >= cnt_c, which
+  // pad the ring -- return zeros without touching memory.
+  auto page_rsrc = [&](const uint16_t* base, int j, int cnt_c) {
+    int nbytes = 0;
+    const uint16_t* ptr = base;
+    if (j < cnt_c) {
+      const int pid = __builtin_amdgcn_readlane(pids, j);
+      const int valid = min(16, n - (first + (kc + j) * NW) * 16);
+      nbytes = valid * D * 2;
+      ptr = base + int64_t(pid) * page_stride;
+    }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ptr), (short)0, nbytes,
+                                             kBufferFlags);
+  };
+  auto issue = [&](int j, int cnt_c, uint4 (&kk)[NL], uint4 (&vv)[NL]) {
+    const auto kr = page_rsrc(kbase, j, cnt_c);
+    const auto vr = page_rsrc(vbase, j, cnt_c);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        kk[i] = load16(kp + i * 512);
-        vv[i] = load16(vp + i * 512);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const bool ok = i * TPI + r < valid;
-        kk[i] = ok ? load16(kp + i * 512) : zero4();
-        vv[i] = ok ? load16(vp + i * 512) : zero4();
-      }
+    for (int i = 0; i < NL; ++i) {
+      kk[i] = buffer_load16(kr, lane * 16 + i * 1024);
+      vv[i] = buffer_load16(vr, lane * 16 + i * 1024);
     }
   };
 
-  auto compute_page = [&](int k, const uint4 (&kk)[NL], const uint4 (&vv)[NL]) {
-    const int valid = n - (first + k * NW) * 16;
+  auto compute_page = [&](int j, const uint4 (&kk)[NL], const uint4 (&vv)[NL]) {
+    const int valid = n - (first + (kc + j) * NW) * 16;
     float x[NL][GP];
 #pragma unroll
     for (int i = 0; i < NL; ++i)
@@ -182,17 +191,22 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
     }
   };
 
-  if (cnt > 0) {
-    uint4 kc[NL], vc[NL];
-    load_page(0, kc, vc);
-    for (int k = 0; k < cnt; ++k) {
-      uint4 kn[NL], vn[NL];
-      if (k + 1 < cnt) load_page(k + 1, kn, vn);
-      compute_page(k, kc, vc);
+  // Register ring of R = PF + 1 pages: page j + PF is in flight while page j
+  // is computed.  The steady-state loop has no loads under a branch, so the
+  // compiler's in-order vmcnt waits keep PF pages outstanding.
+  constexpr int R = PF + 1;
+  uint4 kb[R][NL], vb[R][NL];
+  for (kc = 0; kc < cnt; kc += 64) {
+    const int cnt_c = min(64, cnt - kc);
+    pids = (lane < cnt_c) ? bt[first + (kc + lane) * NW] : 0;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        kc[i] = kn[i];
-        vc[i] = vn[i];
+    for (int u = 0; u < PF; ++u) issue(u, cnt_c, kb[u], vb[u]);
+    for (int j0 = 0; j0 < cnt_c; j0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int j = j0 + u;
+        issue(j + PF, cnt_c, kb[(u + PF) % R], vb[(u + PF) % R]);
+        if (j < cnt_c) compute_page(j, kb[u], vb[u]);
       }
     }
   }
@@ -262,17 +276,17 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
   }
 }
 
-template <int D, int GP, bool BF16, int NW>
+template <int D, int GP, bool BF16, int NW, int PF>
 pkv_status launch_valu_modes(int mode, const SplitArgs& a, int grid, hipStream_t s) {
   const dim3 block(NW * 64);
   if (mode == kModeWorkqueue)
-    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, kModeWorkqueue>), dim3(grid), block, 0,
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeWorkqueue>), dim3(grid), block, 0,
                        s, a);
   else if (mode == kModeBucket)
-    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, kModeBucket>), dim3(grid), block, 0, s,
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeBucket>), dim3(grid), block, 0, s,
                        a);
   else
-    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, kModeNoSplit>), dim3(grid), block, 0,
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeNoSplit>), dim3(grid), block, 0,
                        s, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
@@ -280,10 +294,10 @@ pkv_status launch_valu_modes(int mode, const SplitArgs& a, int grid, hipStream_t
 template <int D, bool BF16>
 pkv_status launch_valu_g(int gp, int mode, const SplitArgs& a, int grid, hipStream_t s) {
   switch (gp) {
-    case 1: return launch_valu_modes<D, 1, BF16, 8>(mode, a, grid, s);
-    case 2: return launch_valu_modes<D, 2, BF16, 8>(mode, a, grid, s);
-    case 4: return launch_valu_modes<D, 4, BF16, 8>(mode, a, grid, s);
-    case 8: return launch_valu_modes<D, 8, BF16, 4>(mode, a, grid, s);
+    case 1: return launch_valu_modes<D, 1, BF16, 8, 2>(mode, a, grid, s);
+    case 2: return launch_valu_modes<D, 2, BF16, 8, 2>(mode, a, grid, s);
+    case 4: return launch_valu_modes<D, 4, BF16, 8, 2>(mode, a, grid, s);
+    case 8: return launch_valu_modes<D, 8, BF16, 4, 2>(mode, a, grid, s);
     default: return PKV_ESHAPE;
   }
 }

@@ -17,7 +17,16 @@ pytestmark = pytest.mark.gpu
 
 SEED = traces.HELD_OUT_SEED
 PATHS = ("bucketed", "workqueue", "nosplit")
-KERNELS = ("valu",)
+KERNELS = ("valu", "mfma")
+
+
+def _applicable(kernel, d, group):
+    """The matrix-core kernel covers d = 128 (any G <= 16); the vector-ALU
+    kernel covers d = 64 and 128 with G <= 8."""
+    if kernel == "mfma" and d != 128:
+        pytest.skip("matrix-core kernel is d=128 only")
+    if kernel == "valu" and group > 8:
+        pytest.skip("vector-ALU kernel is G<=8 only")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -40,6 +49,7 @@ def _run(w, path, splits, kernel):
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("path", PATHS)
 def test_tiny_config_all_paths(path, kernel):
+    _applicable(kernel, 64, 4)
     w = traces.generate(traces.get_spec("tiny"), SEED)
     say(f"[tiny] path={path} kernel={kernel}")
     ref_out, ref_lse = oracle_out(w)
@@ -51,13 +61,14 @@ def test_tiny_config_all_paths(path, kernel):
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("path", ("workqueue", "bucketed"))
 def test_split_states_match_oracle(path, kernel):
-    spec = traces.custom_spec(3, 8, 2, 64, splits=5)
+    d = 128 if kernel == "mfma" else 64
+    spec = traces.custom_spec(3, 8, 2, d, splits=5)
     lens = np.array([200, 37, 0], dtype=np.int32)
     w = traces.generate(spec, SEED, seq_lens=lens)
     say(f"[states] path={path} kernel={kernel}")
     step, _ = _run(w, path, 5, kernel)
     a = traces.oracle_arrays(w)
-    plan = oracle.plan(lens, 2, 8, 64, 16, 5, path)
+    plan = oracle.plan(lens, 2, 8, d, 16, 5, path)
     m, l, o = oracle.split_states_for_plan(a["q"], a["k_pool"], a["v_pool"], a["block_table"],
                                            plan.tasks, a["scale"], 16, "f16", 4, lens)
     gm = step.st_m.cpu().numpy().astype(np.float64)
@@ -140,9 +151,10 @@ EDGE_LENS = np.array([0, 1, 15, 16, 17, 33, 100, 0, 250], dtype=np.int32)
 
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("d", (64, 128))
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (6, 2), (12, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (6, 2), (12, 2), (32, 2)])
 @pytest.mark.parametrize("dtype", ("f16", "bf16"))
 def test_edge_lengths_shapes_and_dtypes(d, hq, hkv, dtype, kernel):
+    _applicable(kernel, d, hq // hkv)
     spec = traces.custom_spec(len(EDGE_LENS), hq, hkv, d, splits=3, dtype=dtype)
     w = traces.generate(spec, SEED, seq_lens=EDGE_LENS)
     say(f"[edge] d={d} hq={hq} hkv={hkv} {dtype} kernel={kernel}")
