@@ -20,9 +20,7 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
-import statistics
 import sys
 import time
 
@@ -56,68 +54,6 @@ def describe(spec, path, splits, lens):
     return (f"{spec.name}: B={spec.batch} Hq={spec.num_q_heads} Hkv={spec.num_kv_heads} "
             f"d={spec.head_dim} P={spec.page_size} S={splits} {spec.dtype} path={path} "
             f"N={'/'.join(str(int(n)) for n in lens) if len(lens) <= 8 else f'{len(lens)} rows'}")
-
-
-def time_engine(w, wd, path, splits, kernel, steps, warmup, copies_gib):
-    """Device-time a path; returns a dict of timings and counters."""
-    import torch
-
-    from paged_kv_gqa_block_amd import engine
-
-    prob = engine.problem_from_workload(w, kernel)
-    step = engine.DecodeStep(prob, path, splits)
-    stream = torch.cuda.current_stream()
-    info = step.plan(wd["seq_lens_host"], stream=stream)
-    pool_bytes = wd["k_pool"].numel() * 2 * 2
-    n_copies = max(1, min(64, math.ceil(copies_gib * (1 << 30) / pool_bytes)))
-    pools = [(wd["k_pool"], wd["v_pool"])]
-    for _ in range(n_copies - 1):
-        pools.append((wd["k_pool"].clone(), wd["v_pool"].clone()))
-    views = [dict(wd, k_pool=k, v_pool=v) for k, v in pools]
-    torch.cuda.synchronize()
-
-    for i in range(warmup):
-        step.run(views[i % n_copies], stream)
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        e = ev[i]
-        v = views[(warmup + i) % n_copies]
-        e[0].record(stream)
-        step.decode(v, stream)
-        e[1].record(stream)
-        step.merge(stream)
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    split_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
-
-    # Synchronised wall time including policy-free host planning + H2D.
-    sync_us = []
-    for i in range(min(steps, 20)):
-        v = views[i % n_copies]
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        step.plan(wd["seq_lens_host"], stream=stream)
-        step.run(v, stream)
-        torch.cuda.synchronize()
-        sync_us.append((time.perf_counter() - t) * 1e6)
-
-    n_split = {0: info.n_buckets, 1: 1 if info.n_tasks else 0, 2: 1}[info.path]
-    return {
-        "info": info.as_dict(),
-        "n_split_launches": n_split,
-        "step_us_mean": 1e3 * statistics.fmean(step_ms),
-        "step_us_median": 1e3 * statistics.median(step_ms),
-        "split_us_mean": 1e3 * statistics.fmean(split_ms),
-        "wall_ms_per_step": 1e3 * wall / steps,
-        "sync_wall_us_median": statistics.median(sync_us),
-        "n_copies": n_copies,
-        "out": step.out,
-    }
 
 
 def cpu_baseline(w, budget_s):
@@ -167,7 +103,7 @@ def main(argv=None):
     import numpy as np
     import torch
 
-    from paged_kv_gqa_block_amd import engine, traces
+    from paged_kv_gqa_block_amd import engine, timing, traces
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     spec = traces.get_spec(args.config)
@@ -182,11 +118,12 @@ def main(argv=None):
     wd = engine.to_device(w)
     engine.validate_inputs(wd)
 
-    r = time_engine(w, wd, path, splits, args.kernel, args.steps, args.warmup, args.copies_gib)
+    views = timing.pool_copies(wd, args.copies_gib)
+    r = timing.time_path(w, views, path, splits, args.kernel, args.steps, args.warmup)
     info = r["info"]
     kv = info["kv_bytes"]
-    gbs = kv / (r["step_us_mean"] * 1e-6) / 1e9
-    split_launch_us = r["split_us_mean"] / max(1, r["n_split_launches"])
+    gbs = kv / (r["step_us"] * 1e-6) / 1e9
+    split_launch_us = r["split_us"] / max(1, r["n_split_launches"])
     split_gbs = (kv / max(1, r["n_split_launches"])) / (split_launch_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
@@ -196,7 +133,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["wall_ms_per_step"], 4),
-        "us_per_step": round(r["step_us_mean"], 2),
+        "us_per_step": round(r["step_us"], 2),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "higher_is_better": True,
         "scaling": "weak",
@@ -207,7 +144,7 @@ def main(argv=None):
                    "kernel": args.kernel, "path": path, "splits": splits,
                    "launches_per_step": info["n_launches"], "n_tasks": info["n_tasks"],
                    "kv_bytes": kv, "merge_state_bytes": info["merge_state_bytes"],
-                   "pool_copies_rotated": r["n_copies"],
+                   "pool_copies_rotated": len(views),
                    "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None,

@@ -139,10 +139,13 @@ typedef struct pkv_policy_table {
  *   [16+2B ..]         row_nsplit[B]
  *   [16+3B ..]         row_task_off[B+1] (first task of each row in task
  *                      order; entry B = n_tasks)
- *   tasks[n_tasks][4]  { row, (kv_head << 16) | split, page_begin, page_end }
- *                      starting at word [10], a multiple of 4
- *                      ordered (row, kv_head, split); WORKQUEUE: the state
- *                      slot of task j is j
+ *   tasks[n_tasks][4]  { row, (kv_head << 16) | split, page_begin, token_end }
+ *                      with token_end = min(page_end * P, N_row) (so
+ *                      page_end = ceil(token_end / P)), starting at word
+ *                      [10], a multiple of 4
+ *                      ordered (row, kv_head, split) for WORKQUEUE and
+ *                      NOSPLIT, bucket by bucket for BUCKETED; WORKQUEUE:
+ *                      the state slot of task j is j
  *   buckets[n_buckets][8] { length, pages, pages_per_split, nsplit, n_rows,
  *                           first index into bucket rows, 0, 0 }
  *                      ascending length; BUCKETED state slot of

@@ -230,6 +230,7 @@ def decode_plan(plan_host) -> dict:
     n_tasks, n_buckets = int(w[6]), int(w[7])
     ot, ob, obr = int(w[10]), int(w[11]), int(w[12])
     tasks = w[ot:ot + 4 * n_tasks].reshape(-1, 4)
+    psz = int(w[14])
     return {
         "path": PATH_NAMES[int(w[1])],
         "batch": b,
@@ -241,8 +242,9 @@ def decode_plan(plan_host) -> dict:
         "row_pages": w[h + b:h + 2 * b].tolist(),
         "row_nsplit": w[h + 2 * b:h + 3 * b].tolist(),
         "row_task_off": w[h + 3 * b:h + 4 * b + 1].tolist(),
-        "tasks": [(int(t[0]), int(t[1]) >> 16, int(t[1]) & 0xFFFF, int(t[2]), int(t[3]))
-                  for t in tasks],
+        "tasks": [(int(t[0]), int(t[1]) >> 16, int(t[1]) & 0xFFFF, int(t[2]),
+                   -(-int(t[3]) // psz)) for t in tasks],
+        "task_token_end": [int(t[3]) for t in tasks],
         "buckets": [tuple(int(x) for x in w[ob + 8 * k:ob + 8 * k + 8]) for k in range(n_buckets)],
         "bucket_rows": w[obr:obr + b].tolist() if n_buckets else [],
         "total_words": int(w[13]),

@@ -81,10 +81,12 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
     const int32_t* e = bw + kBucketWords * k;
     const int64_t items = int64_t(e[4]) * prob->num_kv_heads * w[kSplits];
     if (items > INT32_MAX) return PKV_ERANGE;
+    a.bucket_len = e[0];
     a.bucket_pages = e[1];
     a.bucket_pps = e[2];
     a.bucket_nsplit = e[3];
     a.bucket_rows = dev + w[kOffBucketRows] + e[5];
+    a.bucket_row0 = (e[4] == 1) ? w[w[kOffBucketRows] + e[5]] : -1;
     a.num_items = static_cast<int32_t>(items);
     st = launch_split(*prob, kModeBucket, prob->kernel, a, static_cast<int>(items), stream);
     if (st != PKV_OK) return st;
@@ -121,12 +123,14 @@ extern "C" pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host,
     a.row_task_off = dev + PKV_PLAN_HEADER_WORDS + 3 * b;
     a.num_rows = b;
     a.mode = kModeWorkqueue;
+    a.bucket_row0 = -1;
     return launch_merge(*prob, a, stream);
   }
   const int32_t* bw = w + w[kOffBuckets];
   for (int k = 0; k < w[kNumBuckets]; ++k) {
     const int32_t* e = bw + kBucketWords * k;
     a.bucket_rows = dev + w[kOffBucketRows] + e[5];
+    a.bucket_row0 = (e[4] == 1) ? w[w[kOffBucketRows] + e[5]] : -1;
     a.num_rows = e[4];
     a.mode = kModeBucket;
     st = launch_merge(*prob, a, stream);

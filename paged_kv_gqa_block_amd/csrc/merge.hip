@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     nsplit = a.row_nsplit[row];
     base = int64_t(a.row_task_off[row]) + int64_t(g) * nsplit;
   } else {
-    row = a.bucket_rows[ri];
+    row = (a.bucket_row0 >= 0) ? a.bucket_row0 : a.bucket_rows[ri];
     nsplit = a.splits;
     base = (int64_t(row) * hkv + g) * a.splits;
   }
@@ -141,12 +141,15 @@ pkv_status launch_split_valu(const pkv_problem& p, int mode, const SplitArgs& a,
 pkv_status launch_split_mfma(const pkv_problem& p, int mode, const SplitArgs& a, int grid,
                              hipStream_t s);
 
-// Chooses the split-kernel arithmetic.  AUTO currently means the vector-ALU
-// kernel; the matrix-core kernel (d = 128) is selected explicitly.
+// Chooses the split-kernel arithmetic.  AUTO takes the matrix-core kernel
+// wherever it applies (d = 128, any G <= 16) -- on MI355X it is faster than the
+// vector-ALU kernel on every measured workload -- and the vector-ALU kernel for
+// d = 64 (G <= 8).
 pkv_status launch_split(const pkv_problem& p, int mode, int kernel, const SplitArgs& a, int grid,
                         hipStream_t s) {
   if (grid <= 0) return PKV_OK;
-  if (kernel == PKV_KERNEL_MFMA) return launch_split_mfma(p, mode, a, grid, s);
+  if (kernel == PKV_KERNEL_MFMA || (kernel == PKV_KERNEL_AUTO && p.head_dim == 128))
+    return launch_split_mfma(p, mode, a, grid, s);
   return launch_split_valu(p, mode, a, grid, s);
 }
 

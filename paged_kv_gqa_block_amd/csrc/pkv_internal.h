@@ -44,7 +44,7 @@ struct SplitArgs {
   const void* v_pool;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  const int32_t* tasks;        // workqueue: tasks[n][4]
+  const int32_t* tasks;        // workqueue: tasks[n][4] {row, g<<16|s, page_begin, tok_end}
   const int32_t* bucket_rows;  // bucket: rows of this bucket
   float* st_m;
   float* st_l;
@@ -58,7 +58,9 @@ struct SplitArgs {
   int32_t bucket_pps;
   int32_t bucket_nsplit;
   int32_t bucket_pages;
-  int32_t num_items;  // grid items (tasks, bucket slots or rows * Hkv)
+  int32_t bucket_len;   // bucket: the rows' common length N_b
+  int32_t bucket_row0;  // bucket: its only row when it has one, else -1
+  int32_t num_items;    // grid items (tasks, bucket slots or rows * Hkv)
   float scale_log2;   // sm_scale * log2(e)
 };
 
@@ -76,6 +78,7 @@ struct MergeArgs {
   int32_t splits;     // bucket slot stride S
   int32_t num_rows;   // rows covered by this launch
   int32_t mode;       // kModeWorkqueue or kModeBucket
+  int32_t bucket_row0;  // bucket: its only row when it has one, else -1
 };
 
 // Kernel launchers (HIP translation units).  Return PKV_OK or PKV_EHIP.

@@ -100,12 +100,14 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
   int32_t n_buckets = 0;
   std::vector<int32_t> order;
 
+  // Word 3 is the task's token end min(pe * P, N_row), from which the
+  // kernels get both the page end and the real tokens of the last page.
   auto push_task = [&](int row, int g, int s, int pb, int pe) {
     int32_t* t = tasks + kTaskWords * n_tasks;
     t[0] = row;
     t[1] = (g << 16) | s;
     t[2] = pb;
-    t[3] = pe;
+    t[3] = static_cast<int32_t>(std::min<int64_t>(int64_t(pe) * psz, seq_lens_host[row]));
     ++n_tasks;
   };
 

@@ -1,0 +1,123 @@
+// Pieces shared by the two split / no-split kernels (vector-ALU and
+// matrix-core): task decoding for the three grid modes, the empty-task
+// outputs, and the final combine of the waves' partial states.
+#pragma once
+
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+// One workgroup's work: row, KV head, first page and one-past-last real token
+// of the page range, and the partial-state slot (split modes).
+struct Task {
+  int row;
+  int g;
+  int page_begin;
+  int tok_end;  // min(page_end * 16, N_row); page_end = ceil(tok_end / 16)
+  int64_t slot;
+  bool empty;   // bucket slot past the bucket's split count
+};
+
+template <int MODE>
+__device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
+  Task t;
+  const int hkv = a.num_kv_heads;
+  t.empty = false;
+  t.slot = 0;
+  if constexpr (MODE == kModeWorkqueue) {
+    const int4 w = reinterpret_cast<const int4*>(a.tasks)[item];
+    t.row = w.x;
+    t.g = w.y >> 16;
+    t.page_begin = w.z;
+    t.tok_end = w.w;
+    t.slot = item;
+  } else if constexpr (MODE == kModeBucket) {
+    const int s = item % a.splits;
+    const int rest = item / a.splits;
+    t.g = rest % hkv;
+    t.row = (a.bucket_row0 >= 0) ? a.bucket_row0 : a.bucket_rows[rest / hkv];
+    t.slot = (int64_t(t.row) * hkv + t.g) * a.splits + s;
+    t.empty = s >= a.bucket_nsplit;
+    t.page_begin = s * a.bucket_pps;
+    const int pe = min(t.page_begin + a.bucket_pps, a.bucket_pages);
+    t.tok_end = min(pe * 16, a.bucket_len);
+  } else {
+    t.row = item / hkv;
+    t.g = item - t.row * hkv;
+    t.page_begin = 0;
+    t.tok_end = -1;  // filled in from seq_lens by the caller
+  }
+  return t;
+}
+
+// Neutral state (-inf, 0, 0) of an empty bucket slot.
+template <int NW>
+__device__ __forceinline__ void write_neutral(const SplitArgs& a, const Task& t, int G, int D) {
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) a.st_o[t.slot * G * D + e] = 0.f;
+  if (threadIdx.x < G) {
+    a.st_m[t.slot * G + threadIdx.x] = kNegInf;
+    a.st_l[t.slot * G + threadIdx.x] = 0.f;
+  }
+}
+
+// Output of an empty row on the no-split path: out = 0, lse = -inf.
+template <int NW>
+__device__ __forceinline__ void write_empty_row(const SplitArgs& a, const Task& t, int G, int D) {
+  uint16_t* out =
+      static_cast<uint16_t*>(a.out) + (int64_t(t.row) * a.num_q_heads + t.g * G) * D;
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) out[e] = 0;
+  if (a.lse && threadIdx.x < G)
+    a.lse[int64_t(t.row) * a.num_q_heads + t.g * G + threadIdx.x] = kNegInf;
+}
+
+// Combine the NW waves' states (max in log2 units, sum, unnormalised output,
+// already in LDS) and write either the task's partial state or, on the
+// no-split path, the normalised output and lse.  Must follow a barrier.
+template <int D, int GP, int NW, bool BF16, int MODE>
+__device__ __forceinline__ void combine_waves_and_store(const SplitArgs& a, const Task& t, int G,
+                                                        const float (&sm_m)[NW][GP],
+                                                        const float (&sm_l)[NW][GP],
+                                                        const float (&sm_o)[NW][GP][D]) {
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+    const int h = e / D;
+    const int dd = e - h * D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    float lsum = 0.f, osum = 0.f;
+    if (mx != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w][h];
+        const float wt = (mw == kNegInf) ? 0.f : fast_exp2(mw - mx);
+        lsum = fmaf(wt, sm_l[w][h], lsum);
+        osum = fmaf(wt, sm_o[w][h][dd], osum);
+      }
+    }
+    if constexpr (MODE == kModeNoSplit) {
+      const int64_t qh = int64_t(t.row) * a.num_q_heads + t.g * G + h;
+      const float val = (lsum > 0.f) ? osum / lsum : 0.f;
+      static_cast<uint16_t*>(a.out)[qh * D + dd] = Elem<BF16>::from_float(val);
+      if (dd == 0 && a.lse) a.lse[qh] = (lsum > 0.f) ? mx * kLn2 + __logf(lsum) : kNegInf;
+    } else {
+      a.st_o[(t.slot * G + h) * D + dd] = osum;
+      if (dd == 0) {
+        a.st_m[t.slot * G + h] = (mx == kNegInf) ? kNegInf : mx * kLn2;
+        a.st_l[t.slot * G + h] = lsum;
+      }
+    }
+  }
+}
+
+// Block-table entries of 64 of a wave's pages: lane j holds the pool page of
+// the wave's page k0 + j (its pages are first, first + NW, ...).  Entries past
+// the task's pages are read only while inside the table row, and never used.
+template <int NW>
+__device__ __forceinline__ int load_page_ids(const int32_t* bt_row, int max_pages, int first,
+                                             int k0, int lane) {
+  const int idx = first + (k0 + lane) * NW;
+  return (idx < max_pages) ? bt_row[idx] : 0;
+}
+
+}  // namespace pkv

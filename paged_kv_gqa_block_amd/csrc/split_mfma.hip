@@ -31,8 +31,7 @@
 // Method: PersistentKV summary pages, "Methodology / 1. Native block-table
 // decode engine" (GQA over paged KV read through the block table, partial
 // online-softmax state per disjoint split, empty splits write neutral state).
-#include "device_common.h"
-#include "pkv_internal.h"
+#include "split_common.h"
 
 namespace pkv {
 namespace {
@@ -137,50 +136,28 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
   __shared__ float sm_o[NW][GP][D];
   __shared__ uint4 sm_k[NW][16][16];  // per-wave K tile: [token][physical chunk]
 
-  // ---- task (identical to the vector-ALU kernel) ---------------------------
-  const int item = blockIdx.x;
-  int row, g, pb, pe;
-  int64_t slot = 0;
-  if constexpr (MODE == kModeWorkqueue) {
-    const int4 t = reinterpret_cast<const int4*>(a.tasks)[item];
-    row = t.x;
-    g = t.y >> 16;
-    pb = t.z;
-    pe = t.w;
-    slot = item;
-  } else if constexpr (MODE == kModeBucket) {
-    const int s = item % a.splits;
-    const int rest = item / a.splits;
-    g = rest % hkv;
-    row = a.bucket_rows[rest / hkv];
-    slot = (int64_t(row) * hkv + g) * a.splits + s;
-    if (s >= a.bucket_nsplit) {  // empty split: neutral state, exit early
-      for (int e = threadIdx.x; e < G * D; e += NW * 64) a.st_o[slot * G * D + e] = 0.f;
-      if (threadIdx.x < G) {
-        a.st_m[slot * G + threadIdx.x] = kNegInf;
-        a.st_l[slot * G + threadIdx.x] = 0.f;
-      }
+  // ---- task --------------------------------------------------------------
+  Task tk = decode_task<MODE>(a, blockIdx.x);
+  if constexpr (MODE == kModeBucket) {
+    if (tk.empty) {  // empty split: neutral state, exit early
+      write_neutral<NW>(a, tk, G, D);
       return;
     }
-    pb = s * a.bucket_pps;
-    pe = min(pb + a.bucket_pps, a.bucket_pages);
-  } else {
-    row = item / hkv;
-    g = item % hkv;
-    pb = 0;
-    pe = 0;
   }
-  const int n = a.seq_lens[row];
+  const int row = tk.row, g = tk.g, pb = tk.page_begin;
+  const int32_t* bt = a.block_table + int64_t(row) * a.max_pages;
+  const int first = pb + wave;  // this wave's pages: first, first + NW, ...
+  // Page ids of the first 64 of them; issued before the row length is known.
+  int pids = load_page_ids<NW>(bt, a.max_pages, first, 0, lane);
   if constexpr (MODE == kModeNoSplit) {
-    pe = (n + 15) >> 4;
-    if (pe == 0) {
-      uint16_t* out = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.num_q_heads + g * G) * D;
-      for (int e = threadIdx.x; e < G * D; e += NW * 64) out[e] = 0;
-      if (a.lse && threadIdx.x < G) a.lse[int64_t(row) * a.num_q_heads + g * G + threadIdx.x] =
-          kNegInf;
+    tk.tok_end = a.seq_lens[row];
+    if (tk.tok_end == 0) {  // empty row: zero output, lse = -inf
+      write_empty_row<NW>(a, tk, G, D);
       return;
     }
   }
+  const int tok_end = tk.tok_end;
+  const int pe = (tok_end + 15) >> 4;
 
   // B operand of the score MFMAs: lane (kg, c) holds elements
   // [32t + 8kg, 32t + 8kg + 8) of head c for MFMA t (zero for padded heads).
@@ -205,19 +182,16 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
   const int64_t page_stride = int64_t(hkv) * 16 * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + int64_t(g) * 16 * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + int64_t(g) * 16 * D;
-  const int32_t* bt = a.block_table + int64_t(row) * a.max_pages;
   const float sl2 = a.scale_log2;
-  const int first = pb + wave;
   const int cnt = (pe > first) ? (pe - first + NW - 1) / NW : 0;
 
   int kc = 0;
-  int pids = 0;
   auto page_rsrc = [&](const uint16_t* base, int j, int cnt_c) {
     int nbytes = 0;
     const uint16_t* ptr = base;
     if (j < cnt_c) {
       const int pid = __builtin_amdgcn_readlane(pids, j);
-      const int valid = min(16, n - (first + (kc + j) * NW) * 16);
+      const int valid = min(16, tok_end - (first + (kc + j) * NW) * 16);
       nbytes = valid * D * 2;
       ptr = base + int64_t(pid) * page_stride;
     }
@@ -235,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
   };
 
   auto compute_page = [&](int j, const uint4 (&kk)[NL], const uint4 (&vv)[NL]) {
-    const int valid = n - (first + (kc + j) * NW) * 16;
+    const int valid = tok_end - (first + (kc + j) * NW) * 16;
     // K page -> LDS tile (token kg + 4i, chunk c), then back in A order.
     uint4 (&tile)[16][16] = sm_k[wave];
 #pragma unroll
@@ -303,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
   uint4 kb[R][NL], vb[R][NL];
   for (kc = 0; kc < cnt; kc += 64) {
     const int cnt_c = min(64, cnt - kc);
-    pids = (lane < cnt_c) ? bt[first + (kc + lane) * NW] : 0;
+    if (kc > 0) pids = load_page_ids<NW>(bt, a.max_pages, first, kc, lane);
 #pragma unroll
     for (int u = 0; u < PF; ++u) issue(u, cnt_c, kb[u], vb[u]);
     for (int j0 = 0; j0 < cnt_c; j0 += R) {
@@ -334,36 +308,8 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
   }
   __syncthreads();
 
-  // ---- merge the waves and write (identical to the vector-ALU kernel) ------
-  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-    const int h = e / D;
-    const int dd = e - h * D;
-    float mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
-    float lsum = 0.f, osum = 0.f;
-    if (mx != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = sm_m[w][h];
-        const float wt = (mw == kNegInf) ? 0.f : fast_exp2(mw - mx);
-        lsum = fmaf(wt, sm_l[w][h], lsum);
-        osum = fmaf(wt, sm_o[w][h][dd], osum);
-      }
-    }
-    if constexpr (MODE == kModeNoSplit) {
-      const int64_t qh = int64_t(row) * a.num_q_heads + g * G + h;
-      const float val = (lsum > 0.f) ? osum / lsum : 0.f;
-      static_cast<uint16_t*>(a.out)[qh * D + dd] = Elem<BF16>::from_float(val);
-      if (dd == 0 && a.lse) a.lse[qh] = (lsum > 0.f) ? mx * kLn2 + __logf(lsum) : kNegInf;
-    } else {
-      a.st_o[(slot * G + h) * D + dd] = osum;
-      if (dd == 0) {
-        a.st_m[slot * G + h] = (mx == kNegInf) ? kNegInf : mx * kLn2;
-        a.st_l[slot * G + h] = lsum;
-      }
-    }
-  }
+  // ---- merge the waves and write ------------------------------------------
+  combine_waves_and_store<D, GP, NW, BF16, MODE>(a, tk, G, sm_m, sm_l, sm_o);
 }
 
 template <int GP, bool BF16, int NW, int PF>

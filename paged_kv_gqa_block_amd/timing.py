@@ -1,0 +1,87 @@
+"""Device timing of one decode path (HIP events on the launch stream).
+
+Used by bench.py and by the policy calibration.  A step is the engine's
+device work for one decode step of one layer (split + merge launches, or the
+single no-split launch) with the plan resident on the GPU.  Every step reads
+the next of several copies of the KV pools, so the 256 MB Infinity Cache
+cannot serve K/V from the previous step (consecutive layers of a model also
+read different pools).
+"""
+from __future__ import annotations
+
+import math
+import statistics
+import time
+
+import torch
+
+from . import engine
+
+
+def pool_copies(wd: dict, copies_gib: float, max_copies: int = 64):
+    """Views of the workload on n copies of the pools (n * pool size >= copies_gib)."""
+    pool_bytes = wd["k_pool"].numel() * wd["k_pool"].element_size() * 2
+    n = max(1, min(max_copies, math.ceil(copies_gib * (1 << 30) / pool_bytes)))
+    views = [wd]
+    for _ in range(n - 1):
+        views.append(dict(wd, k_pool=wd["k_pool"].clone(), v_pool=wd["v_pool"].clone()))
+    return views
+
+
+def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", steps: int = 50,
+              warmup: int = 10, sync_reps: int = 20) -> dict:
+    """Times one (path, split cap).  Returns step / split times and counters."""
+    wd = views[0]
+    prob = engine.problem_from_workload(w, kernel)
+    step = engine.DecodeStep(prob, path, splits)
+    stream = torch.cuda.current_stream()
+    info = step.plan(wd["seq_lens_host"], stream=stream)
+    n = len(views)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        step.run(views[i % n], stream)
+    torch.cuda.synchronize()
+
+    # K back-to-back steps between two events (no event between launches).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step.run(views[(warmup + i) % n], stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = 1e3 * e0.elapsed_time(e1) / steps
+
+    # Split launches alone, back to back, so event overhead is amortised.
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for i in range(steps):
+        step.decode(views[(warmup + steps + i) % n], stream)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    split_us = 1e3 * e2.elapsed_time(e3) / steps
+
+    # Synchronised wall time per step including host planning and the plan
+    # upload (the pages' end-to-end latency metric).
+    sync_us = []
+    for i in range(sync_reps):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        step.plan(wd["seq_lens_host"], stream=stream)
+        step.run(views[i % n], stream)
+        torch.cuda.synchronize()
+        sync_us.append((time.perf_counter() - t) * 1e6)
+
+    n_split = {0: info.n_buckets, 1: 1 if info.n_tasks else 0, 2: 1}[info.path]
+    return {
+        "path": path,
+        "splits": splits,
+        "info": info.as_dict(),
+        "n_split_launches": n_split,
+        "step_us": step_us,
+        "split_us": split_us,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "sync_wall_us_median": statistics.median(sync_us) if sync_us else None,
+        "out": step.out,
+    }

@@ -32,6 +32,7 @@ import torch
 
 CALIBRATION_SEED = 20260622
 HELD_OUT_SEED = 20260623
+POLICY_BATCHES = (1, 2, 4, 8, 16, 32, 64)
 
 _TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -74,9 +75,14 @@ def _spec_table():
         "uniform": WorkloadSpec("uniform", 8, 32, 8, 128, 16, "uniform", 32, "f16",
                                 lo=1024, hi=32768),
     }
-    for b in (1, 2, 4, 8, 16, 32, 64):
+    for b in POLICY_BATCHES:
+        # Policy sweep: 64/8 heads, d=128, bf16, U[1024,32768].
         specs[f"policy_b{b}"] = WorkloadSpec(f"policy_b{b}", b, 64, 8, 128, 16, "uniform", 32,
                                              "bf16", lo=1024, hi=32768)
+        # Short-context band of the same shape, U[64,2048], so the calibrated
+        # table also has an N_max split.
+        specs[f"policy_short_b{b}"] = WorkloadSpec(f"policy_short_b{b}", b, 64, 8, 128, 16,
+                                                   "uniform", 32, "bf16", lo=64, hi=2048)
     return specs
 
 
