@@ -29,6 +29,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention µs/step and achieved HBM GB/s (% of peak), paged GQA"
 HBM_PEAK_GBS = 8000.0
+# Counter-based HBM traffic of the split kernel per workload (rocprofv3
+# FETCH_SIZE + WRITE_SIZE runs, scaled against a copy kernel); reported only
+# while the kernel sources still hash to the value recorded with it.
+TRAFFIC_PROFILES = {"long": "profiles/split_mfma_long_b1_n32768_traffic.txt"}
+KERNEL_SOURCES = ("split_mfma.hip", "split_common.h", "device_common.h", "pkv_internal.h")
 DEFAULT_PATH = {"tiny": "workqueue", "long": "bucketed", "bimodal": "workqueue",
                 "zipf": "workqueue", "uniform": "workqueue"}
 
@@ -54,6 +59,33 @@ def describe(spec, path, splits, lens):
     return (f"{spec.name}: B={spec.batch} Hq={spec.num_q_heads} Hkv={spec.num_kv_heads} "
             f"d={spec.head_dim} P={spec.page_size} S={splits} {spec.dtype} path={path} "
             f"N={'/'.join(str(int(n)) for n in lens) if len(lens) <= 8 else f'{len(lens)} rows'}")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_gqa_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(config: str, kernel_used: str):
+    """Traffic bytes per split launch from profiles/, or None if absent or stale."""
+    rel = TRAFFIC_PROFILES.get(config)
+    if rel is None or kernel_used != "mfma":
+        return None
+    try:
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines()
+                  if line.startswith(("kernel_source_sha256_16:", "traffic_bytes_per_launch:")))
+    if fields.get("kernel_source_sha256_16", "").split()[0:1] != [kernel_source_hash()]:
+        return None
+    return int(fields["traffic_bytes_per_launch"].strip())
 
 
 def cpu_baseline(w, budget_s):
@@ -118,6 +150,9 @@ def main(argv=None):
     wd = engine.to_device(w)
     engine.validate_inputs(wd)
 
+    kernel_used = args.kernel
+    if kernel_used == "auto":  # the library's AUTO rule: matrix cores for d = 128
+        kernel_used = "mfma" if spec.head_dim == 128 else "valu"
     views = timing.pool_copies(wd, args.copies_gib)
     r = timing.time_path(w, views, path, splits, args.kernel, args.steps, args.warmup)
     info = r["info"]
@@ -147,8 +182,11 @@ def main(argv=None):
                    "pool_copies_rotated": len(views),
                    "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "split decode", "launch_us": round(split_launch_us, 2)},
+                     "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args.config, kernel_used),
+                     "kernel": f"split decode ({kernel_used})",
+                     "launch_us": round(split_launch_us, 2),
+                     "algorithmic_bytes_per_launch": kv // max(1, r["n_split_launches"])},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
