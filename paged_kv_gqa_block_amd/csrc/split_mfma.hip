@@ -327,13 +327,17 @@ pkv_status launch_mfma_modes(int mode, const SplitArgs& a, int grid, hipStream_t
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
+// 4 waves per workgroup with one page in flight per wave (140 VGPRs): up to
+// three workgroups share a CU, so one task's start-up overlaps another's
+// streaming.  Measured on MI355X against 8 waves and/or two pages in flight:
+// equal on one long row, 5-8 % faster on batched workloads.
 template <bool BF16>
 pkv_status launch_mfma_g(int gp, int mode, const SplitArgs& a, int grid, hipStream_t s) {
   switch (gp) {
-    case 1: return launch_mfma_modes<1, BF16, 8, 2>(mode, a, grid, s);
-    case 2: return launch_mfma_modes<2, BF16, 8, 2>(mode, a, grid, s);
-    case 4: return launch_mfma_modes<4, BF16, 8, 2>(mode, a, grid, s);
-    case 8: return launch_mfma_modes<8, BF16, 8, 2>(mode, a, grid, s);
+    case 1: return launch_mfma_modes<1, BF16, 4, 1>(mode, a, grid, s);
+    case 2: return launch_mfma_modes<2, BF16, 4, 1>(mode, a, grid, s);
+    case 4: return launch_mfma_modes<4, BF16, 4, 1>(mode, a, grid, s);
+    case 8: return launch_mfma_modes<8, BF16, 4, 1>(mode, a, grid, s);
     case 16: return launch_mfma_modes<16, BF16, 4, 2>(mode, a, grid, s);
     default: return PKV_ESHAPE;
   }
