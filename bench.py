@@ -52,6 +52,10 @@ def parse_args(argv=None):
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--copies-gib", type=float, default=1.0,
                    help="total size of the rotated KV pool copies")
+    p.add_argument("--all", action="store_true",
+                   help="instead of the single contract line, print one JSON line per "
+                        "(workload, path) for every workload, each with a short CPU-oracle "
+                        "sample")
     return p.parse_args(argv)
 
 
@@ -126,6 +130,52 @@ def cpu_baseline(w, budget_s):
             "us_per_step_equiv": dt / max(done_bytes, 1) * sum(kv_row_bytes) * 1e6}
 
 
+ALL_CONFIGS = ("tiny", "long", "bimodal", "zipf", "uniform") + tuple(
+    f"policy_b{b}" for b in (1, 2, 4, 8, 16, 32, 64))
+
+
+def run_all(args) -> int:
+    """Every workload x every path (+ the policy's choice), oracle timed beside."""
+    import torch
+
+    from paged_kv_gqa_block_amd import engine, timing, traces
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    rules = engine.load_policy_table()
+    for name in ALL_CONFIGS:
+        spec = traces.get_spec(name)
+        w = traces.generate(spec, traces.HELD_OUT_SEED)
+        lens = w["seq_lens"].numpy()
+        wd = engine.to_device(w)
+        engine.validate_inputs(wd)
+        views = timing.pool_copies(wd, args.copies_gib, max_copies=8)
+        pol = engine.choose(rules, spec.batch, int(lens.max()))
+        cands = [("bucketed", spec.splits), ("workqueue", spec.splits), ("nosplit", 1)]
+        if pol not in cands:
+            cands.append(pol)
+        cpu = None if args.no_cpu_baseline else cpu_baseline(w, min(args.cpu_budget_s, 5.0))
+        for path, s in cands:
+            r = timing.time_path(w, views, path, s, args.kernel, args.steps, args.warmup,
+                                 sync_reps=5)
+            kv = r["info"]["kv_bytes"]
+            gbs = kv / (r["step_us"] * 1e-6) / 1e9
+            print(json.dumps({
+                "workload": describe(spec, path, s, lens), "config": name, "path": path,
+                "splits": s, "policy_choice": (path, s) == pol,
+                "us_per_step": round(r["step_us"], 2), "GB/s": round(gbs, 1),
+                "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                "split_us_per_launch": round(r["split_us"] / max(1, r["n_split_launches"]), 2),
+                "launches_per_step": r["info"]["n_launches"], "kv_bytes": kv,
+                "merge_state_bytes": r["info"]["merge_state_bytes"],
+                "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1),
+                "cpu_oracle": None if cpu is None else {
+                    "GB/s": round(cpu["value"], 3), "us_per_step": round(cpu["us_per_step_equiv"]),
+                    "cores": cpu["cores"]}}), flush=True)
+        del views, wd, w
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -138,6 +188,8 @@ def main(argv=None):
     from paged_kv_gqa_block_amd import engine, timing, traces
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.all:
+        return run_all(args)
     spec = traces.get_spec(args.config)
     seed = traces.HELD_OUT_SEED if args.seed is None else args.seed
     path = args.path or DEFAULT_PATH.get(args.config, "workqueue")
@@ -154,7 +206,8 @@ def main(argv=None):
     if kernel_used == "auto":  # the library's AUTO rule: matrix cores for d = 128
         kernel_used = "mfma" if spec.head_dim == 128 else "valu"
     views = timing.pool_copies(wd, args.copies_gib)
-    r = timing.time_path(w, views, path, splits, args.kernel, args.steps, args.warmup)
+    # The contract line times exactly K steps once (repeats=1).
+    r = timing.time_path(w, views, path, splits, args.kernel, args.steps, args.warmup, repeats=1)
     info = r["info"]
     kv = info["kv_bytes"]
     gbs = kv / (r["step_us"] * 1e-6) / 1e9

@@ -69,7 +69,7 @@ def measure(spec: traces.WorkloadSpec, seed: int, configs, steps: int, warmup: i
     views = timing.pool_copies(wd, 1.0, max_copies=8)
     out = {}
     for path, s in configs:
-        r = timing.time_path(w, views, path, s, "auto", steps, warmup, sync_reps=5)
+        r = timing.time_path(w, views, path, s, "auto", steps, warmup, sync_reps=0, repeats=5)
         out[f"{path}:{s}"] = round(r["step_us"], 2)
         log(f"  {name} seed={seed} {path:9s} S={s:2d}: {r['step_us']:9.2f} us/step")
     n_max = int(w["seq_lens"].max())

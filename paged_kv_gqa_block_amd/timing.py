@@ -29,8 +29,12 @@ def pool_copies(wd: dict, copies_gib: float, max_copies: int = 64):
 
 
 def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", steps: int = 50,
-              warmup: int = 10, sync_reps: int = 20) -> dict:
-    """Times one (path, split cap).  Returns step / split times and counters."""
+              warmup: int = 10, sync_reps: int = 20, repeats: int = 5) -> dict:
+    """Times one (path, split cap).  Returns step / split times and counters.
+
+    The timed loops run `repeats` times; the reported step and split times are
+    the medians (short kernels vary by several percent from run to run).
+    """
     wd = views[0]
     prob = engine.problem_from_workload(w, kernel)
     step = engine.DecodeStep(prob, path, splits)
@@ -42,25 +46,31 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         step.run(views[i % n], stream)
     torch.cuda.synchronize()
 
-    # K back-to-back steps between two events (no event between launches).
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
-        step.run(views[(warmup + i) % n], stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_us = 1e3 * e0.elapsed_time(e1) / steps
+    step_runs, split_runs, walls = [], [], []
+    for rep in range(repeats):
+        # K back-to-back steps between two events (no event between launches).
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        base = warmup + rep * 2 * steps
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            step.run(views[(base + i) % n], stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        step_runs.append(1e3 * e0.elapsed_time(e1) / steps)
 
-    # Split launches alone, back to back, so event overhead is amortised.
-    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e2.record(stream)
-    for i in range(steps):
-        step.decode(views[(warmup + steps + i) % n], stream)
-    e3.record(stream)
-    torch.cuda.synchronize()
-    split_us = 1e3 * e2.elapsed_time(e3) / steps
+        # Split launches alone, back to back, so event overhead is amortised.
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        for i in range(steps):
+            step.decode(views[(base + steps + i) % n], stream)
+        e3.record(stream)
+        torch.cuda.synchronize()
+        split_runs.append(1e3 * e2.elapsed_time(e3) / steps)
+    step_us = statistics.median(step_runs)
+    split_us = statistics.median(split_runs)
+    wall = statistics.median(walls)
 
     # Synchronised wall time per step including host planning and the plan
     # upload (the pages' end-to-end latency metric).
@@ -81,6 +91,7 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         "n_split_launches": n_split,
         "step_us": step_us,
         "split_us": split_us,
+        "step_us_runs": [round(x, 2) for x in step_runs],
         "wall_ms_per_step": 1e3 * wall / steps,
         "sync_wall_us_median": statistics.median(sync_us) if sync_us else None,
         "out": step.out,
