@@ -217,6 +217,40 @@ pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void*
                      float* lse, hipStream_t stream);
 
 /*
+ * Device-planned workqueue step (no host round trip, graph-capturable).
+ *
+ * pkv_plan_device builds the WORKQUEUE plan on the GPU from the device copy
+ * of the row lengths, in the same layout (and with the same contents, for
+ * valid lengths) as pkv_plan(..., PKV_WORKQUEUE, ...).  plan_bytes must be at
+ * least pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits).  Lengths cannot be
+ * checked on the host: a row whose length lies outside
+ * [0, max_pages_per_row * P] is planned as an empty row, and the number of
+ * such rows is written to *bad_rows_dev when it is not NULL.
+ *
+ * pkv_decode_device runs the split kernel as a persistent grid (two
+ * workgroups per compute unit, at most B * Hkv * max_splits) whose workgroups
+ * stride over the device-built task list; the task count is read on the
+ * device.  It writes st_m, st_l, st_o exactly as pkv_decode does for the
+ * WORKQUEUE path (slot = task index); the state buffers must hold
+ * B * Hkv * max_splits slots.  Matrix-core kernel only: head_dim 128, and
+ * kernel PKV_KERNEL_AUTO or PKV_KERNEL_MFMA (else PKV_ESHAPE).
+ *
+ * pkv_merge_device combines the states into out / lse (lse may be NULL) using
+ * the device plan's row arrays.  The three calls are ordered on `stream`.
+ * Errors as pkv_plan / pkv_decode / pkv_merge.
+ */
+pkv_status pkv_plan_device(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                           int32_t max_splits, void* plan_dev, size_t plan_bytes,
+                           int32_t* bad_rows_dev, hipStream_t stream);
+pkv_status pkv_decode_device(const pkv_problem* prob, const void* plan_dev, int32_t max_splits,
+                             const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, float* st_m, float* st_l, float* st_o,
+                             hipStream_t stream);
+pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan_dev, const float* st_m,
+                            const float* st_l, const float* st_o, void* out, float* lse,
+                            hipStream_t stream);
+
+/*
  * Calibrated path choice: first rule of `table` matching (batch, max_len).
  * Writes the rule's path and split cap.  Errors: PKV_EINVAL (null pointer,
  * negative n_rules, a rule with an unknown path or splits < 1),

@@ -36,7 +36,8 @@ DTYPE_IDS = {"f16": PKV_F16, "bf16": PKV_BF16}
 KERNEL_IDS = {"auto": PKV_KERNEL_AUTO, "valu": PKV_KERNEL_VALU, "mfma": PKV_KERNEL_MFMA}
 
 EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pkv_merge",
-            "pkv_policy", "pkv_status_str")
+            "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_policy",
+            "pkv_status_str")
 
 
 class PkvError(RuntimeError):
@@ -102,6 +103,12 @@ def _load() -> ctypes.CDLL:
     lib.pkv_decode.restype = i32
     lib.pkv_merge.argtypes = [prob_p, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.pkv_merge.restype = i32
+    lib.pkv_plan_device.argtypes = [prob_p, vp, i32, vp, ctypes.c_size_t, vp, vp]
+    lib.pkv_plan_device.restype = i32
+    lib.pkv_decode_device.argtypes = [prob_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.pkv_decode_device.restype = i32
+    lib.pkv_merge_device.argtypes = [prob_p, vp, vp, vp, vp, vp, vp, vp]
+    lib.pkv_merge_device.restype = i32
     lib.pkv_policy.argtypes = [ctypes.POINTER(pkv_policy_table), i32, i32,
                                ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.pkv_policy.restype = i32
@@ -208,6 +215,29 @@ def pkv_merge(prob: pkv_problem, plan_host, plan_dev, st_m, st_l, st_o, out, lse
     _check("pkv_merge", LIB.pkv_merge(
         ctypes.byref(prob), _ptr(plan_host), _ptr(plan_dev), _ptr(st_m), _ptr(st_l),
         _ptr(st_o), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def pkv_plan_device(prob: pkv_problem, seq_lens_dev, max_splits: int, plan_dev,
+                    plan_bytes: int | None = None, bad_rows_dev=None, stream=None) -> None:
+    if plan_bytes is None:
+        plan_bytes = plan_dev.numel() * plan_dev.element_size()
+    _check("pkv_plan_device", LIB.pkv_plan_device(
+        ctypes.byref(prob), _ptr(seq_lens_dev), max_splits, _ptr(plan_dev), plan_bytes,
+        _ptr(bad_rows_dev), _stream(stream)))
+
+
+def pkv_decode_device(prob: pkv_problem, plan_dev, max_splits: int, q, k_pool, v_pool,
+                      block_table, st_m, st_l, st_o, stream=None) -> None:
+    _check("pkv_decode_device", LIB.pkv_decode_device(
+        ctypes.byref(prob), _ptr(plan_dev), max_splits, _ptr(q), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), _ptr(st_m), _ptr(st_l), _ptr(st_o), _stream(stream)))
+
+
+def pkv_merge_device(prob: pkv_problem, plan_dev, st_m, st_l, st_o, out, lse=None,
+                     stream=None) -> None:
+    _check("pkv_merge_device", LIB.pkv_merge_device(
+        ctypes.byref(prob), _ptr(plan_dev), _ptr(st_m), _ptr(st_l), _ptr(st_o), _ptr(out),
+        _ptr(lse), _stream(stream)))
 
 
 def pkv_policy(rules, batch: int, max_len: int):

@@ -20,7 +20,9 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["planner.cpp", "api.cpp", "merge.hip", "split_valu.hip", "split_mfma.hip"]
+SOURCES = [
+    "planner.cpp", "api.cpp", "merge.hip", "split_valu.hip", "split_mfma.hip", "planner_device.hip",
+]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", f"-I{INCLUDE}", f"-I{CSRC}",

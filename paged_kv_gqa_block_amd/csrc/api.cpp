@@ -1,6 +1,7 @@
 // Public entry points pkv_decode, pkv_merge, pkv_policy and pkv_status_str:
 // argument validation on the host, then kernel launches on the caller's
 // stream.  The planner entry points live in planner.cpp.
+#include <algorithm>
 #include <cmath>
 
 #include "pkv_internal.h"
@@ -137,6 +138,91 @@ extern "C" pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host,
     if (st != PKV_OK) return st;
   }
   return PKV_OK;
+}
+
+// ---- device-planned workqueue step ----------------------------------------
+
+namespace {
+
+int32_t off_tasks_words(int32_t batch) {
+  return (PKV_PLAN_HEADER_WORDS + 4 * batch + 1 + 3) & ~3;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_plan_device(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                                      int32_t max_splits, void* plan_dev, size_t plan_bytes,
+                                      int32_t* bad_rows_dev, hipStream_t stream) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  if (!seq_lens_dev || !plan_dev) return PKV_EINVAL;
+  if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
+  if (plan_bytes < pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits)) return PKV_ENOSPC;
+  return launch_plan_device(*prob, seq_lens_dev, max_splits, static_cast<int32_t*>(plan_dev),
+                            bad_rows_dev, stream);
+}
+
+extern "C" pkv_status pkv_decode_device(const pkv_problem* prob, const void* plan_dev,
+                                        int32_t max_splits, const void* q, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_table,
+                                        float* st_m, float* st_l, float* st_o,
+                                        hipStream_t stream) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  if (!plan_dev || !q || !k_pool || !v_pool || !block_table || !st_m || !st_l || !st_o)
+    return PKV_EINVAL;
+  if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
+  if (prob->head_dim != 128 || prob->kernel == PKV_KERNEL_VALU) return PKV_ESHAPE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return PKV_EHIP;
+  const int32_t* plan = static_cast<const int32_t*>(plan_dev);
+  SplitArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.st_m = st_m;
+  a.st_l = st_l;
+  a.st_o = st_o;
+  a.num_q_heads = prob->num_q_heads;
+  a.num_kv_heads = prob->num_kv_heads;
+  a.max_pages = prob->max_pages_per_row;
+  a.splits = max_splits;
+  a.scale_log2 = prob->sm_scale * kLog2e;
+  a.tasks = plan + off_tasks_words(prob->batch);
+  a.n_tasks_dev = plan + kNumTasks;
+  a.bucket_row0 = -1;
+  // Two resident workgroups per CU, never more than the largest task count.
+  const int64_t upper = int64_t(prob->batch) * prob->num_kv_heads * max_splits;
+  const int grid = static_cast<int>(std::min<int64_t>(upper, 2 * int64_t(cus)));
+  a.num_items = grid;
+  return launch_split(*prob, kModePersistent, prob->kernel, a, grid, stream);
+}
+
+extern "C" pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan_dev,
+                                       const float* st_m, const float* st_l, const float* st_o,
+                                       void* out, float* lse, hipStream_t stream) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  if (!plan_dev || !st_m || !st_l || !st_o || !out) return PKV_EINVAL;
+  const int32_t* plan = static_cast<const int32_t*>(plan_dev);
+  const int b = prob->batch;
+  MergeArgs a{};
+  a.st_m = st_m;
+  a.st_l = st_l;
+  a.st_o = st_o;
+  a.out = out;
+  a.lse = lse;
+  a.num_q_heads = prob->num_q_heads;
+  a.num_kv_heads = prob->num_kv_heads;
+  a.row_nsplit = plan + PKV_PLAN_HEADER_WORDS + 2 * b;
+  a.row_task_off = plan + PKV_PLAN_HEADER_WORDS + 3 * b;
+  a.num_rows = b;
+  a.mode = kModeWorkqueue;
+  a.bucket_row0 = -1;
+  return launch_merge(*prob, a, stream);
 }
 
 extern "C" pkv_status pkv_policy(const pkv_policy_table* table, int32_t batch, int32_t max_len,

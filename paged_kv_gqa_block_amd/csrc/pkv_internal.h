@@ -34,7 +34,7 @@ constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 16;
 
 // Which grid a split-kernel launch walks.
-enum SplitMode : int { kModeWorkqueue = 0, kModeBucket = 1, kModeNoSplit = 2 };
+enum SplitMode : int { kModeWorkqueue = 0, kModeBucket = 1, kModeNoSplit = 2, kModePersistent = 3 };
 
 // Everything a split / no-split kernel needs; passed by value as a kernel
 // argument.  Pointers are device pointers.
@@ -45,6 +45,7 @@ struct SplitArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* tasks;        // workqueue: tasks[n][4] {row, g<<16|s, page_begin, tok_end}
+  const int32_t* n_tasks_dev;  // persistent: task count, read on the device
   const int32_t* bucket_rows;  // bucket: rows of this bucket
   float* st_m;
   float* st_l;
@@ -85,6 +86,8 @@ struct MergeArgs {
 pkv_status launch_split(const pkv_problem& prob, int mode, int kernel, const SplitArgs& args,
                         int grid, hipStream_t stream);
 pkv_status launch_merge(const pkv_problem& prob, const MergeArgs& args, hipStream_t stream);
+pkv_status launch_plan_device(const pkv_problem& prob, const int32_t* seq_lens_dev, int32_t splits,
+                              int32_t* plan_dev, int32_t* bad_rows_dev, hipStream_t stream);
 
 // Shape checks shared by plan / decode / merge.
 pkv_status check_problem(const pkv_problem* prob);

@@ -119,8 +119,19 @@ struct Pv<true> {  // bf16 P and V
   }
 };
 
+// LDS of one workgroup: the waves' partial states and each wave's K tile.
+template <int GP, int NW>
+struct MfmaShared {
+  float m[NW][GP];
+  float l[NW][GP];
+  float o[NW][GP][128];
+  uint4 k[NW][16][16];  // per-wave K tile: [token][physical chunk]
+};
+
+// One task (row, KV head, page range): stream its pages, then combine the
+// waves and write the partial state (or, no-split, the normalised output).
 template <int GP, bool BF16, int NW, int PF, int MODE>
-__global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
+__device__ __forceinline__ void mfma_task(const SplitArgs& a, Task tk, MfmaShared<GP, NW>& sh) {
   constexpr int D = 128;
   constexpr int NL = 4;      // 16-byte loads per page per pool (4 tokens each)
   constexpr int HR = (GP + 3) / 4;  // MFMA output row groups holding real heads
@@ -130,20 +141,11 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
   const int kg = lane >> 4;  // row group: tokens kg + 4i
   const int hkv = a.num_kv_heads;
   const int G = a.num_q_heads / hkv;
+  auto& sm_m = sh.m;
+  auto& sm_l = sh.l;
+  auto& sm_o = sh.o;
+  auto& sm_k = sh.k;
 
-  __shared__ float sm_m[NW][GP];
-  __shared__ float sm_l[NW][GP];
-  __shared__ float sm_o[NW][GP][D];
-  __shared__ uint4 sm_k[NW][16][16];  // per-wave K tile: [token][physical chunk]
-
-  // ---- task --------------------------------------------------------------
-  Task tk = decode_task<MODE>(a, blockIdx.x);
-  if constexpr (MODE == kModeBucket) {
-    if (tk.empty) {  // empty split: neutral state, exit early
-      write_neutral<NW>(a, tk, G, D);
-      return;
-    }
-  }
   const int row = tk.row, g = tk.g, pb = tk.page_begin;
   const int32_t* bt = a.block_table + int64_t(row) * a.max_pages;
   const int first = pb + wave;  // this wave's pages: first, first + NW, ...
@@ -312,6 +314,30 @@ __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
   combine_waves_and_store<D, GP, NW, BF16, MODE>(a, tk, G, sm_m, sm_l, sm_o);
 }
 
+// Grid modes: one workgroup per workqueue task / bucket slot / (row, KV head);
+// or persistent: a fixed grid striding over a device-built workqueue whose
+// task count is read from the plan on the device.
+template <int GP, bool BF16, int NW, int PF, int MODE>
+__global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
+  __shared__ MfmaShared<GP, NW> sh;
+  if constexpr (MODE == kModePersistent) {
+    const int n_tasks = *a.n_tasks_dev;
+    for (int t = blockIdx.x; t < n_tasks; t += gridDim.x) {
+      mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, decode_task<kModeWorkqueue>(a, t), sh);
+      __syncthreads();  // LDS is reused by the next task
+    }
+  } else {
+    const Task tk = decode_task<MODE>(a, blockIdx.x);
+    if constexpr (MODE == kModeBucket) {
+      if (tk.empty) {  // empty split: neutral state, exit early
+        write_neutral<NW>(a, tk, a.num_q_heads / a.num_kv_heads, 128);
+        return;
+      }
+    }
+    mfma_task<GP, BF16, NW, PF, MODE>(a, tk, sh);
+  }
+}
+
 template <int GP, bool BF16, int NW, int PF>
 pkv_status launch_mfma_modes(int mode, const SplitArgs& a, int grid, hipStream_t s) {
   const dim3 block(NW * 64);
@@ -321,9 +347,12 @@ pkv_status launch_mfma_modes(int mode, const SplitArgs& a, int grid, hipStream_t
   else if (mode == kModeBucket)
     hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeBucket>), dim3(grid), block, 0, s,
                        a);
-  else
+  else if (mode == kModeNoSplit)
     hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeNoSplit>), dim3(grid), block, 0,
                        s, a);
+  else
+    hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModePersistent>), dim3(grid), block,
+                       0, s, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

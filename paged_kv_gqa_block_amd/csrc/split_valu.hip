@@ -229,9 +229,11 @@ pkv_status launch_valu_modes(int mode, const SplitArgs& a, int grid, hipStream_t
   else if (mode == kModeBucket)
     hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeBucket>), dim3(grid), block, 0, s,
                        a);
-  else
+  else if (mode == kModeNoSplit)
     hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeNoSplit>), dim3(grid), block, 0,
                        s, a);
+  else
+    return PKV_ESHAPE;
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

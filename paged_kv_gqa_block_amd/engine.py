@@ -14,8 +14,9 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import (PATH_IDS, PATH_NAMES, PKV_NOSPLIT, make_problem, pkv_decode, pkv_merge,
-                   pkv_plan, pkv_plan_bytes, pkv_policy)
+from ._lib import (PATH_IDS, PATH_NAMES, PKV_NOSPLIT, PKV_WORKQUEUE, make_problem, pkv_decode,
+                   pkv_decode_device, pkv_merge, pkv_merge_device, pkv_plan, pkv_plan_bytes,
+                   pkv_plan_device, pkv_policy)
 
 TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
 POLICY_TABLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "policy_table.json")
@@ -81,6 +82,45 @@ class DecodeStep:
     def run(self, w: dict, stream=None):
         self.decode(w, stream)
         self.merge(stream)
+        return self.out, self.lse
+
+
+class DeviceStep:
+    """Device-planned workqueue step: plan, split and merge all on the GPU.
+
+    ``run`` enqueues pkv_plan_device -> pkv_decode_device -> pkv_merge_device on
+    one stream with no host work, so the three launches can be captured once in
+    a HIP graph and replayed while the device lengths change.
+    """
+
+    def __init__(self, prob: _lib.pkv_problem, splits: int, device="cuda"):
+        self.prob = prob
+        self.splits = int(splits)
+        self.device = torch.device(device)
+        nbytes = pkv_plan_bytes(prob, PKV_WORKQUEUE, self.splits)
+        if nbytes == 0:
+            raise _lib.PkvError("pkv_plan_bytes", _lib.PKV_EINVAL, "invalid problem")
+        self.plan_dev = torch.zeros(nbytes // 4, dtype=torch.int32, device=self.device)
+        self.bad_rows = torch.zeros(1, dtype=torch.int32, device=self.device)
+        g = prob.num_q_heads // prob.num_kv_heads
+        d = prob.head_dim
+        dt = torch.bfloat16 if prob.dtype == _lib.PKV_BF16 else torch.float16
+        slots = prob.batch * prob.num_kv_heads * self.splits
+        self.out = torch.empty(prob.batch, prob.num_q_heads, d, dtype=dt, device=self.device)
+        self.lse = torch.empty(prob.batch, prob.num_q_heads, dtype=torch.float32,
+                               device=self.device)
+        self.st_m = torch.empty(slots, g, dtype=torch.float32, device=self.device)
+        self.st_l = torch.empty(slots, g, dtype=torch.float32, device=self.device)
+        self.st_o = torch.empty(slots, g, d, dtype=torch.float32, device=self.device)
+
+    def run(self, w: dict, stream=None):
+        pkv_plan_device(self.prob, w["seq_lens"], self.splits, self.plan_dev,
+                        bad_rows_dev=self.bad_rows, stream=stream)
+        pkv_decode_device(self.prob, self.plan_dev, self.splits, w["q"], w["k_pool"],
+                          w["v_pool"], w["block_table"], self.st_m, self.st_l, self.st_o,
+                          stream=stream)
+        pkv_merge_device(self.prob, self.plan_dev, self.st_m, self.st_l, self.st_o, self.out,
+                         self.lse, stream=stream)
         return self.out, self.lse
 
 

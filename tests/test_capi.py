@@ -203,3 +203,32 @@ def test_status_strings():
     for s in range(-6, 1):
         assert _lib.pkv_status_str(s)
     assert _lib.pkv_status_str(-99) == "unknown status"
+
+
+def test_device_plan_entry_points_validate_before_launch():
+    prob = _prob(2)
+    fake = 0x1000  # never dereferenced: every call below fails validation first
+    need = _lib.pkv_plan_bytes(prob, PKV_WORKQUEUE, 8)
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_plan_device(prob, None, 8, fake, need)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_plan_device(prob, fake, 8, fake, need - 4)
+    assert e.value.status == PKV_ENOSPC
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_plan_device(prob, fake, 0, fake, need)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:  # d = 64 has no persistent kernel
+        _lib.pkv_decode_device(_prob(2, d=64), fake, 8, fake, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ESHAPE
+    valu = _prob(2)
+    valu.kernel = _lib.PKV_KERNEL_VALU
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_decode_device(valu, fake, 8, fake, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ESHAPE
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_decode_device(prob, fake, 8, fake, None, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_merge_device(prob, fake, fake, fake, fake, None)
+    assert e.value.status == PKV_EINVAL
