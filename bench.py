@@ -136,6 +136,7 @@ ALL_CONFIGS = ("tiny", "long", "bimodal", "zipf", "uniform") + tuple(
 
 def run_all(args) -> int:
     """Every workload x every path (+ the policy's choice), oracle timed beside."""
+    import numpy as np
     import torch
 
     from paged_kv_gqa_block_amd import engine, timing, traces
@@ -154,6 +155,21 @@ def run_all(args) -> int:
         if pol not in cands:
             cands.append(pol)
         cpu = None if args.no_cpu_baseline else cpu_baseline(w, min(args.cpu_budget_s, 5.0))
+        if spec.head_dim == 128:
+            for graph in (False, True):
+                r = timing.time_device_path(w, views, spec.splits, args.steps, args.warmup,
+                                            sync_reps=5, graph=graph)
+                kv = int(lens.astype(np.int64).sum()) * spec.num_kv_heads * spec.head_dim * 4
+                gbs = kv / (r["step_us"] * 1e-6) / 1e9
+                print(json.dumps({
+                    "workload": describe(spec, r["path"], spec.splits, lens), "config": name,
+                    "path": r["path"], "splits": spec.splits, "policy_choice": False,
+                    "us_per_step": round(r["step_us"], 2), "GB/s": round(gbs, 1),
+                    "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                    "split_us_per_launch": None, "launches_per_step": 3, "kv_bytes": kv,
+                    "merge_state_bytes": None,
+                    "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1),
+                    "cpu_oracle": None}), flush=True)
         for path, s in cands:
             r = timing.time_path(w, views, path, s, args.kernel, args.steps, args.warmup,
                                  sync_reps=5)

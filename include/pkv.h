@@ -222,15 +222,19 @@ pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void*
  * pkv_plan_device builds the WORKQUEUE plan on the GPU from the device copy
  * of the row lengths, in the same layout (and with the same contents, for
  * valid lengths) as pkv_plan(..., PKV_WORKQUEUE, ...).  plan_bytes must be at
- * least pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits).  Lengths cannot be
+ * least pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits); batch <= 16384
+ * (else PKV_ERANGE).  Lengths cannot be
  * checked on the host: a row whose length lies outside
  * [0, max_pages_per_row * P] is planned as an empty row, and the number of
  * such rows is written to *bad_rows_dev when it is not NULL.
  *
  * pkv_decode_device runs the split kernel as a persistent grid (two
  * workgroups per compute unit, at most B * Hkv * max_splits) whose workgroups
- * stride over the device-built task list; the task count is read on the
- * device.  It writes st_m, st_l, st_o exactly as pkv_decode does for the
+ * claim tasks of the device-built list through a work counter kept in plan
+ * word [total_words] (just past the task list; pkv_plan_bytes leaves room for
+ * it).  pkv_plan_device zeroes the counter and pkv_merge_device resets it, so
+ * every pkv_decode_device must follow a pkv_plan_device or a pkv_merge_device
+ * on the same plan; calls that overlap on one plan race.  It writes st_m, st_l, st_o exactly as pkv_decode does for the
  * WORKQUEUE path (slot = task index); the state buffers must hold
  * B * Hkv * max_splits slots.  Matrix-core kernel only: head_dim 128, and
  * kernel PKV_KERNEL_AUTO or PKV_KERNEL_MFMA (else PKV_ESHAPE).

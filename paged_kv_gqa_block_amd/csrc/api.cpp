@@ -157,6 +157,7 @@ extern "C" pkv_status pkv_plan_device(const pkv_problem* prob, const int32_t* se
   if (st != PKV_OK) return st;
   if (!seq_lens_dev || !plan_dev) return PKV_EINVAL;
   if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
+  if (prob->batch > kMaxDevicePlanRows) return PKV_ERANGE;
   if (plan_bytes < pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits)) return PKV_ENOSPC;
   return launch_plan_device(*prob, seq_lens_dev, max_splits, static_cast<int32_t*>(plan_dev),
                             bad_rows_dev, stream);
@@ -192,7 +193,9 @@ extern "C" pkv_status pkv_decode_device(const pkv_problem* prob, const void* pla
   a.splits = max_splits;
   a.scale_log2 = prob->sm_scale * kLog2e;
   a.tasks = plan + off_tasks_words(prob->batch);
-  a.n_tasks_dev = plan + kNumTasks;
+  // Task count and work counter (word [total_words], after the task list) are
+  // located from the plan header on the device.
+  a.device_plan = const_cast<int32_t*>(plan);
   a.bucket_row0 = -1;
   // Two resident workgroups per CU, never more than the largest task count.
   const int64_t upper = int64_t(prob->batch) * prob->num_kv_heads * max_splits;
@@ -222,6 +225,7 @@ extern "C" pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan
   a.num_rows = b;
   a.mode = kModeWorkqueue;
   a.bucket_row0 = -1;
+  a.device_plan = const_cast<int32_t*>(plan);  // the merge resets the work counter
   return launch_merge(*prob, a, stream);
 }
 

@@ -48,6 +48,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
   __shared__ float s_m[SG], s_l[SG];
   __shared__ float4 s_o[SG][CH];
+  // The split kernel has finished (stream order): reset the persistent
+  // kernel's work counter for the next step on this plan.
+  if (a.device_plan && item == 0 && t == 0) a.device_plan[a.device_plan[kTotalWords]] = 0;
 
   float mloc = kNegInf, lloc = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

@@ -32,6 +32,7 @@ constexpr int kBucketWords = 8;
 constexpr int kTaskWords = 4;
 constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxDevicePlanRows = 16384;  // batch limit of the device-side planner
 
 // Which grid a split-kernel launch walks.
 enum SplitMode : int { kModeWorkqueue = 0, kModeBucket = 1, kModeNoSplit = 2, kModePersistent = 3 };
@@ -45,7 +46,8 @@ struct SplitArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* tasks;        // workqueue: tasks[n][4] {row, g<<16|s, page_begin, tok_end}
-  const int32_t* n_tasks_dev;  // persistent: task count, read on the device
+  int32_t* device_plan;        // persistent: device-built plan; its task count and the
+                               // work counter at word [kTotalWords] are read on the device
   const int32_t* bucket_rows;  // bucket: rows of this bucket
   float* st_m;
   float* st_l;
@@ -80,6 +82,7 @@ struct MergeArgs {
   int32_t num_rows;   // rows covered by this launch
   int32_t mode;       // kModeWorkqueue or kModeBucket
   int32_t bucket_row0;  // bucket: its only row when it has one, else -1
+  int32_t* device_plan;  // device-planned step: the merge resets its work counter; else null
 };
 
 // Kernel launchers (HIP translation units).  Return PKV_OK or PKV_EHIP.

@@ -10,9 +10,12 @@
 // splits for row i, tasks in (row, kv_head, split) order.
 //
 // One 1024-thread workgroup: a max-reduction for T_max, an exclusive scan of
-// the per-row task counts for the row offsets, then every thread writes the
-// tasks of its rows.  Rows whose length lies outside [0, max_pages * P] are
-// planned as empty and counted in *bad_rows.
+// the per-row task counts (wave scans plus one cross-wave step) for the row
+// offsets, kept in LDS; then task j is written by thread j mod 1024, which
+// finds its row by binary search over the offsets.  Batches of up to
+// kMaxDevicePlanRows rows.  Rows whose length lies outside [0, max_pages * P] are
+// planned as empty and counted in *bad_rows.  The word after the plan is the
+// persistent split kernel's work counter, zeroed here.
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -20,80 +23,114 @@ namespace pkv {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1)
+    x = max(x, __builtin_amdgcn_ds_bpermute(((__lane_id() ^ sh) & 63) << 2, x));
+  return x;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan_i(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute(((lane - sh) & 63) << 2, x);
+    if (lane >= sh) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int valid_len(int n, int64_t cap) { return (n < 0 || n > cap) ? -1 : n; }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_workqueue_kernel(
     const int32_t* __restrict__ seq_lens, int32_t* __restrict__ plan, int32_t* bad_rows, int batch,
     int hkv, int splits, int group, int page_size, int max_pages) {
-  __shared__ int s_scan[kPlanThreads];
-  __shared__ int s_bad;
+  __shared__ int s_off[kMaxDevicePlanRows + 1];  // row task offsets
+  __shared__ int s_wave[kPlanWaves];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   int32_t* row_len = plan + PKV_PLAN_HEADER_WORDS;
   int32_t* row_pages = row_len + batch;
   int32_t* row_nsplit = row_pages + batch;
   int32_t* row_task_off = row_nsplit + batch;
   const int off_tasks = (PKV_PLAN_HEADER_WORDS + 4 * batch + 1 + 3) & ~3;
-  int32_t* tasks = plan + off_tasks;
+  int4* tasks = reinterpret_cast<int4*>(plan + off_tasks);
   const int64_t cap = int64_t(max_pages) * page_size;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
 
-  // Pass 1: lengths, pages, T_max.
+  // Pass 1: this thread's chunk of consecutive rows; T_max and bad rows.
+  const int chunk = (batch + kPlanThreads - 1) / kPlanThreads;
+  const int r0 = min(batch, tid * chunk), r1 = min(batch, r0 + chunk);
   int t_max = 0, bad = 0;
-  for (int i = tid; i < batch; i += kPlanThreads) {
-    int n = seq_lens[i];
-    if (n < 0 || n > cap) {  // planned as an empty row
-      n = 0;
-      ++bad;
-    }
-    const int t = (n + page_size - 1) / page_size;
-    row_len[i] = n;
-    row_pages[i] = t;
-    t_max = max(t_max, t);
+  for (int i = r0; i < r1; ++i) {
+    const int n = valid_len(seq_lens[i], cap);
+    bad += (n < 0);
+    t_max = max(t_max, (max(n, 0) + page_size - 1) / page_size);
   }
-  s_scan[tid] = t_max;
-  if (bad) atomicAdd(&s_bad, bad);
+  t_max = wave_max_i(t_max);
+  if (lane == 0) s_wave[wave] = t_max;
   __syncthreads();
-  for (int d = kPlanThreads / 2; d > 0; d >>= 1) {
-    if (tid < d) s_scan[tid] = max(s_scan[tid], s_scan[tid + d]);
-    __syncthreads();
-  }
-  t_max = s_scan[0];
+  t_max = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) t_max = max(t_max, s_wave[w]);
   const int pps = max(1, (t_max + splits - 1) / splits);
   __syncthreads();
 
-  // Pass 2: per-thread chunk of consecutive rows; exclusive scan of task counts.
-  const int chunk = (batch + kPlanThreads - 1) / kPlanThreads;
-  const int r0 = min(batch, tid * chunk), r1 = min(batch, r0 + chunk);
+  // Pass 2: exclusive scan of per-row task counts (Hkv * splits of the row).
   int local = 0;
-  for (int i = r0; i < r1; ++i) local += hkv * ((row_pages[i] + pps - 1) / pps);
-  s_scan[tid] = local;
-  __syncthreads();
-  for (int d = 1; d < kPlanThreads; d <<= 1) {  // inclusive Hillis-Steele scan
-    const int v = (tid >= d) ? s_scan[tid - d] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
-  int off = s_scan[tid] - local;
-  const int n_tasks = s_scan[kPlanThreads - 1];
-
-  // Pass 3: row arrays and tasks {row, kv_head << 16 | split, page_begin, token_end}.
   for (int i = r0; i < r1; ++i) {
-    const int t = row_pages[i];
+    const int n = max(valid_len(seq_lens[i], cap), 0);
+    local += hkv * (((n + page_size - 1) / page_size + pps - 1) / pps);
+  }
+  const int incl = wave_scan_i(local);
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int base = 0, n_tasks = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    base += (w < wave) ? s_wave[w] : 0;
+    n_tasks += s_wave[w];
+  }
+  int off = base + incl - local;
+  for (int i = r0; i < r1; ++i) {
+    const int n0 = valid_len(seq_lens[i], cap);
+    const int n = max(n0, 0);
+    const int t = (n + page_size - 1) / page_size;
     const int ns = (t + pps - 1) / pps;
-    const int n = row_len[i];
+    row_len[i] = n;
+    row_pages[i] = t;
     row_nsplit[i] = ns;
     row_task_off[i] = off;
-    for (int g = 0; g < hkv; ++g)
-      for (int s = 0; s < ns; ++s) {
-        const int pb = s * pps, pe = min(pb + pps, t);
-        int4* dst = reinterpret_cast<int4*>(tasks) + off;
-        *dst = make_int4(i, (g << 16) | s, pb, min(pe * page_size, n));
-        ++off;
-      }
+    s_off[i] = off;
+    off += hkv * ns;
   }
   if (tid == 0) {
+    s_off[batch] = n_tasks;
     row_task_off[batch] = n_tasks;
+  }
+  __syncthreads();
+
+  // Pass 3: task j goes to the last row whose offset is <= j (rows with no
+  // tasks share their successor's offset), found by binary search in LDS.
+  for (int j = tid; j < n_tasks; j += kPlanThreads) {
+    int lo = 0, hi = batch;  // s_off[lo] <= j < s_off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_off[mid] <= j) lo = mid;
+      else hi = mid;
+    }
+    const int row = lo;
+    const int n = max(valid_len(seq_lens[row], cap), 0);
+    const int t = (n + page_size - 1) / page_size;
+    const int ns = (t + pps - 1) / pps;
+    const int k = j - s_off[row];
+    const int g = k / ns, sp = k - g * ns;
+    const int pb = sp * pps, pe = min(pb + pps, t);
+    tasks[j] = make_int4(row, (g << 16) | sp, pb, min(pe * page_size, n));
+  }
+  if (tid == 0) {
     plan[kMagic] = PKV_PLAN_MAGIC;
     plan[kPath] = PKV_WORKQUEUE;
     plan[kBatch] = batch;
@@ -110,9 +147,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_workqueue_kernel(
     plan[kTotalWords] = off_tasks + kTaskWords * n_tasks;
     plan[kWordPageSize] = page_size;
     plan[kWordGroup] = group;
+    plan[off_tasks + kTaskWords * n_tasks] = 0;  // work counter of the persistent kernel
   }
+  // Bad-row count: per-wave sums, one atomic-free combine.
+  int b = bad;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) b += __builtin_amdgcn_ds_bpermute(((lane ^ sh) & 63) << 2, b);
   __syncthreads();
-  if (tid == 0 && bad_rows) *bad_rows = s_bad;
+  if (lane == 0) s_wave[wave] = b;
+  __syncthreads();
+  if (tid == 0 && bad_rows) {
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) total += s_wave[w];
+    *bad_rows = total;
+  }
 }
 
 }  // namespace

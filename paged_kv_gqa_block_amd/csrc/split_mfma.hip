@@ -315,16 +315,26 @@ __device__ __forceinline__ void mfma_task(const SplitArgs& a, Task tk, MfmaShare
 }
 
 // Grid modes: one workgroup per workqueue task / bucket slot / (row, KV head);
-// or persistent: a fixed grid striding over a device-built workqueue whose
+// or persistent: a fixed grid claiming tasks of a device-built workqueue whose
 // task count is read from the plan on the device.
 template <int GP, bool BF16, int NW, int PF, int MODE>
 __global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
   __shared__ MfmaShared<GP, NW> sh;
   if constexpr (MODE == kModePersistent) {
-    const int n_tasks = *a.n_tasks_dev;
-    for (int t = blockIdx.x; t < n_tasks; t += gridDim.x) {
+    // Workgroups claim tasks from a device-scope counter (zeroed by the
+    // device planner and reset by the device merge), so tasks go to whichever
+    // workgroups are running; every workgroup exits once the counter passes
+    // the task count, and none ever waits on another.
+    __shared__ int s_task;
+    const int n_tasks = a.device_plan[kNumTasks];
+    int32_t* counter = a.device_plan + a.device_plan[kTotalWords];
+    for (;;) {
+      if (threadIdx.x == 0) s_task = atomicAdd(counter, 1);
+      __syncthreads();
+      const int t = s_task;
+      if (t >= n_tasks) break;
       mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, decode_task<kModeWorkqueue>(a, t), sh);
-      __syncthreads();  // LDS is reused by the next task
+      __syncthreads();  // LDS (and s_task) are reused by the next task
     }
   } else {
     const Task tk = decode_task<MODE>(a, blockIdx.x);

@@ -96,3 +96,63 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         "sync_wall_us_median": statistics.median(sync_us) if sync_us else None,
         "out": step.out,
     }
+
+
+def time_device_path(w: dict, views, splits: int, steps: int = 50, warmup: int = 10,
+                     sync_reps: int = 20, repeats: int = 5, graph: bool = False) -> dict:
+    """Times the device-planned workqueue step (plan + persistent split + merge
+    on the GPU, no host work).  With ``graph``, each pool copy's step is
+    captured once in a HIP graph and replayed."""
+    wd = views[0]
+    prob = engine.problem_from_workload(w, "auto")
+    step = engine.DeviceStep(prob, splits)
+    n = len(views)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step.run(views[i % n], stream)
+    torch.cuda.synchronize()
+    graphs = None
+    if graph:
+        graphs = []
+        for v in views:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step.run(v, stream)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def one(i):
+        if graphs is None:
+            step.run(views[i % n], stream)
+        else:
+            graphs[i % n].replay()
+
+    runs = []
+    with torch.cuda.stream(stream):
+        for rep in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                one(warmup + rep * steps + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            runs.append(1e3 * e0.elapsed_time(e1) / steps)
+        sync_us = []
+        for i in range(sync_reps):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            one(i)
+            torch.cuda.synchronize()
+            sync_us.append((time.perf_counter() - t) * 1e6)
+    plan = step.plan_dev.cpu().numpy()
+    return {
+        "path": "workqueue_device" + ("_graph" if graph else ""),
+        "splits": splits,
+        "n_tasks": int(plan[6]),
+        "step_us": statistics.median(runs),
+        "step_us_runs": [round(x, 2) for x in runs],
+        "sync_wall_us_median": statistics.median(sync_us) if sync_us else None,
+        "out": step.out,
+    }

@@ -127,3 +127,22 @@ def test_graph_capture_replays_with_growing_lengths():
         ref_out, ref_lse = oracle_out(w_k)
         check_out(step.out, ref_out, "f16", label=f"graph replay {k}")
         check_lse(step.lse, ref_lse, label=f"graph replay {k}")
+
+
+def test_decode_merge_rerun_without_replanning():
+    """The device merge resets the work counter, so decode + merge can run
+    again on the same device plan and give the same bits."""
+    w = traces.generate(traces.get_spec("bimodal"), SEED)
+    wd = engine.to_device(w)
+    say("[device rerun]")
+    step = engine.DeviceStep(engine.problem_from_workload(w), 32)
+    step.run(wd)
+    torch.cuda.synchronize()
+    first = step.out.clone()
+    for _ in range(2):
+        _lib.pkv_decode_device(step.prob, step.plan_dev, 32, wd["q"], wd["k_pool"], wd["v_pool"],
+                               wd["block_table"], step.st_m, step.st_l, step.st_o)
+        _lib.pkv_merge_device(step.prob, step.plan_dev, step.st_m, step.st_l, step.st_o,
+                              step.out, step.lse)
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), step.out.view(torch.int16))
