@@ -255,6 +255,21 @@ pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan_dev, const
                             hipStream_t stream);
 
 /*
+ * KV append: store the step's new key and value of every row in the paged
+ * pools before attention (the input side of a decode step; not described on
+ * the pages).  k_new, v_new: [B][Hkv][d] in the problem dtype.  positions_dev:
+ * int32 [B], the token position to write for each row (its length before the
+ * step); row i's token p goes to pool page block_table[i][p / P], slot p % P.
+ * A negative position marks an inactive row; positions at or past
+ * max_pages_per_row * P are skipped.  The block-table entry of the written
+ * page must be a valid pool page (undefined behaviour otherwise, as for
+ * pkv_decode).  Errors: PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_EHIP.
+ */
+pkv_status pkv_append_kv(const pkv_problem* prob, const void* k_new, const void* v_new,
+                         const int32_t* block_table, const int32_t* positions_dev, void* k_pool,
+                         void* v_pool, hipStream_t stream);
+
+/*
  * Calibrated path choice: first rule of `table` matching (batch, max_len).
  * Writes the rule's path and split cap.  Errors: PKV_EINVAL (null pointer,
  * negative n_rules, a rule with an unknown path or splits < 1),

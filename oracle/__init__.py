@@ -18,6 +18,8 @@ what the PersistentKV summary pages define:
   launches per step).
 * ``policy`` -- first-match calibrated threshold table keyed on (B, N_max)
   ("2. Calibrated adaptive policy").
+* ``append_kv`` -- storing a step's new key/value through the block table
+  (the input side of the decode step; not described on the pages).
 """
 from .attention import (  # noqa: F401
     attention,
@@ -29,5 +31,6 @@ from .attention import (  # noqa: F401
     split_state,
     split_states_for_plan,
 )
+from .append import append_kv  # noqa: F401
 from .planner import plan, pages_of  # noqa: F401
 from .policy import choose  # noqa: F401

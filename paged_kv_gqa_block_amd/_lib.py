@@ -36,8 +36,8 @@ DTYPE_IDS = {"f16": PKV_F16, "bf16": PKV_BF16}
 KERNEL_IDS = {"auto": PKV_KERNEL_AUTO, "valu": PKV_KERNEL_VALU, "mfma": PKV_KERNEL_MFMA}
 
 EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pkv_merge",
-            "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_policy",
-            "pkv_status_str")
+            "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_append_kv",
+            "pkv_policy", "pkv_status_str")
 
 
 class PkvError(RuntimeError):
@@ -109,6 +109,8 @@ def _load() -> ctypes.CDLL:
     lib.pkv_decode_device.restype = i32
     lib.pkv_merge_device.argtypes = [prob_p, vp, vp, vp, vp, vp, vp, vp]
     lib.pkv_merge_device.restype = i32
+    lib.pkv_append_kv.argtypes = [prob_p, vp, vp, vp, vp, vp, vp, vp]
+    lib.pkv_append_kv.restype = i32
     lib.pkv_policy.argtypes = [ctypes.POINTER(pkv_policy_table), i32, i32,
                                ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.pkv_policy.restype = i32
@@ -238,6 +240,13 @@ def pkv_merge_device(prob: pkv_problem, plan_dev, st_m, st_l, st_o, out, lse=Non
     _check("pkv_merge_device", LIB.pkv_merge_device(
         ctypes.byref(prob), _ptr(plan_dev), _ptr(st_m), _ptr(st_l), _ptr(st_o), _ptr(out),
         _ptr(lse), _stream(stream)))
+
+
+def pkv_append_kv(prob: pkv_problem, k_new, v_new, block_table, positions_dev, k_pool, v_pool,
+                  stream=None) -> None:
+    _check("pkv_append_kv", LIB.pkv_append_kv(
+        ctypes.byref(prob), _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(positions_dev),
+        _ptr(k_pool), _ptr(v_pool), _stream(stream)))
 
 
 def pkv_policy(rules, batch: int, max_len: int):

@@ -229,6 +229,27 @@ extern "C" pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan
   return launch_merge(*prob, a, stream);
 }
 
+extern "C" pkv_status pkv_append_kv(const pkv_problem* prob, const void* k_new,
+                                    const void* v_new, const int32_t* block_table,
+                                    const int32_t* positions_dev, void* k_pool, void* v_pool,
+                                    hipStream_t stream) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  if (!k_new || !v_new || !block_table || !positions_dev || !k_pool || !v_pool)
+    return PKV_EINVAL;
+  AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_table = block_table;
+  a.positions = positions_dev;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_kv_heads = prob->num_kv_heads;
+  a.head_dim = prob->head_dim;
+  a.max_pages = prob->max_pages_per_row;
+  return launch_append(a, prob->batch, stream);
+}
+
 extern "C" pkv_status pkv_policy(const pkv_policy_table* table, int32_t batch, int32_t max_len,
                                  int32_t* path_out, int32_t* splits_out) {
   if (!table || !path_out || !splits_out || table->n_rules < 0) return PKV_EINVAL;

@@ -85,10 +85,23 @@ struct MergeArgs {
   int32_t* device_plan;  // device-planned step: the merge resets its work counter; else null
 };
 
+struct AppendArgs {
+  const void* k_new;  // [B][Hkv][d]
+  const void* v_new;
+  const int32_t* block_table;
+  const int32_t* positions;  // [B]: slot to write; < 0 = inactive row
+  void* k_pool;
+  void* v_pool;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_pages;
+};
+
 // Kernel launchers (HIP translation units).  Return PKV_OK or PKV_EHIP.
 pkv_status launch_split(const pkv_problem& prob, int mode, int kernel, const SplitArgs& args,
                         int grid, hipStream_t stream);
 pkv_status launch_merge(const pkv_problem& prob, const MergeArgs& args, hipStream_t stream);
+pkv_status launch_append(const AppendArgs& args, int batch, hipStream_t stream);
 pkv_status launch_plan_device(const pkv_problem& prob, const int32_t* seq_lens_dev, int32_t splits,
                               int32_t* plan_dev, int32_t* bad_rows_dev, hipStream_t stream);
 

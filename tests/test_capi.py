@@ -232,3 +232,16 @@ def test_device_plan_entry_points_validate_before_launch():
     with pytest.raises(PkvError) as e:
         _lib.pkv_merge_device(prob, fake, fake, fake, fake, None)
     assert e.value.status == PKV_EINVAL
+
+
+def test_append_validates_before_launch():
+    prob = _prob(2)
+    fake = 0x1000
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_append_kv(prob, fake, None, fake, fake, fake, fake)
+    assert e.value.status == PKV_EINVAL
+    bad = _prob(2)
+    bad.head_dim = 96
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_append_kv(bad, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ESHAPE

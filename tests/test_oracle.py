@@ -243,3 +243,34 @@ def test_bf16_path_matches_f16_path_on_shared_values():
     o2, l2 = attention(to_bf16_bits(q), to_bf16_bits(kp), to_bf16_bits(vp), bt, np.array(lens),
                        0.5, 4, "bf16")
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_append_oracle_writes_only_the_addressed_slot():
+    rng = np.random.default_rng(11)
+    pool = rng.standard_normal((6, 2, 4, 8)).astype(np.float16)
+    v_pool = rng.standard_normal((6, 2, 4, 8)).astype(np.float16)
+    bt = np.array([[5, 2], [1, 0]], dtype=np.int32)
+    k_new = rng.standard_normal((2, 2, 8)).astype(np.float16)
+    v_new = rng.standard_normal((2, 2, 8)).astype(np.float16)
+    k2, v2 = oracle.append_kv(pool, v_pool, bt, np.array([6, -1]), k_new, v_new, 4)
+    # Position 6 of row 0 = page bt[0][1] = 2, slot 2; row 1 is inactive.
+    assert np.array_equal(k2[2, :, 2], k_new[0]) and np.array_equal(v2[2, :, 2], v_new[0])
+    mask = np.ones(k2.shape[:3], bool)
+    mask[2, :, 2] = False
+    assert np.array_equal(k2[mask], pool[mask]) and np.array_equal(v2[mask], v_pool[mask])
+
+
+def test_append_one_by_one_rebuilds_the_dense_sequence():
+    """Appending tokens 0..N-1 in order reproduces the dense K/V through the table."""
+    rng = np.random.default_rng(12)
+    n, hkv, d, p = 13, 2, 8, 4
+    kd = rng.standard_normal((n, hkv, d)).astype(np.float16)
+    vd = rng.standard_normal((n, hkv, d)).astype(np.float16)
+    bt = np.array([[3, 0, 4, 1]], dtype=np.int32)
+    k = np.full((5, hkv, p, d), np.nan, np.float16)
+    v = np.full_like(k, np.nan)
+    for t in range(n):
+        k, v = oracle.append_kv(k, v, bt, np.array([t]), kd[t][None], vd[t][None], p)
+    got_k, got_v = oracle.gather_row(k, v, bt[0], n, 1, p, "f16")
+    np.testing.assert_array_equal(got_k, kd[:, 1].astype(np.float64))
+    np.testing.assert_array_equal(got_v, vd[:, 1].astype(np.float64))
