@@ -201,3 +201,22 @@ def test_two_runs_are_bit_identical(kernel):
     s1.run(wd)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), s1.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("batch", (32, 64))
+def test_policy_sweep_large_batches_sampled_rows(batch):
+    """Full-size B=32/64 bf16 sweep workloads in the launch configuration the
+    calibrated policy picks (and the three single paths); the oracle checks a
+    sample of rows (first, a middle one, the longest, last)."""
+    w = traces.generate(traces.get_spec(f"policy_b{batch}"), SEED)
+    lens = w["seq_lens"].numpy()
+    rows = sorted({0, batch // 2, int(lens.argmax()), batch - 1})
+    say(f"[policy_b{batch}] sampled rows {rows}")
+    ref_out, ref_lse = oracle_out(w, rows=rows)
+    rules = engine.load_policy_table()
+    chosen = engine.choose(rules, batch, int(lens.max()))
+    for path, s in dict.fromkeys([chosen, ("workqueue", 32), ("bucketed", 32), ("nosplit", 1)]):
+        step, _ = _run(w, path, s, "auto")
+        check_out(step.out, ref_out, "bf16", rows=rows, label=f"policy_b{batch}/{path}:{s}")
+        check_lse(step.lse, ref_lse, rows=rows, label=f"policy_b{batch}/{path}:{s}")
+        assert torch.isfinite(step.out.float()).all()
