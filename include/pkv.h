@@ -80,8 +80,15 @@ enum {
   PKV_BUCKETED = 0,  /* exact-length buckets: per bucket one rectangular
                         rows x Hkv x S split grid and one merge launch      */
   PKV_WORKQUEUE = 1, /* compact 1-D workqueue of non-empty tasks + 1 merge  */
-  PKV_NOSPLIT = 2    /* one single-pass launch, one workgroup per
+  PKV_NOSPLIT = 2,   /* one single-pass launch, one workgroup per
                         (row, kv head), writes the normalised output        */
+  PKV_PADDED = 3     /* power-of-two padded buckets: rows grouped by their
+                        page count rounded up to a power of two, one
+                        rows x Hkv x S split grid and one merge launch per
+                        bucket, split granule from the padded length, but
+                        every row keeps its row-local bound (the pages'
+                        "Row-local bounds": splits past the row's real pages
+                        write neutral state and read no KV)                */
 };
 
 /* Split-kernel arithmetic. AUTO picks the faster one measured on MI355X. */
@@ -105,7 +112,7 @@ typedef struct pkv_problem {
 typedef struct pkv_plan_info {
   int32_t path;
   int32_t n_tasks;          /* non-empty (row, kv head, split) tasks        */
-  int32_t n_buckets;        /* exact-length buckets (BUCKETED), else 0      */
+  int32_t n_buckets;        /* buckets (BUCKETED, PADDED), else 0           */
   int32_t n_launches;       /* kernel launches per step (split + merge)     */
   int32_t n_state_slots;    /* partial-state slots written by the split     */
   int32_t n_empty_slots;    /* slots that only hold a neutral state         */
@@ -144,12 +151,16 @@ typedef struct pkv_policy_table {
  *                      page_end = ceil(token_end / P)), starting at word
  *                      [10], a multiple of 4
  *                      ordered (row, kv_head, split) for WORKQUEUE and
- *                      NOSPLIT, bucket by bucket for BUCKETED; WORKQUEUE:
- *                      the state slot of task j is j
+ *                      NOSPLIT, bucket by bucket for BUCKETED and PADDED;
+ *                      WORKQUEUE: the state slot of task j is j
  *   buckets[n_buckets][8] { length, pages, pages_per_split, nsplit, n_rows,
  *                           first index into bucket rows, 0, 0 }
- *                      ascending length; BUCKETED state slot of
- *                      (row, kv_head, split) is (row * Hkv + kv_head) * S + split
+ *                      BUCKETED: ascending length; PADDED: length = -1 (rows
+ *                      keep their own), pages = the padded page count
+ *                      (0 or a power of two), ascending, nsplit = the
+ *                      padded length's split count (a row's own count is
+ *                      row_nsplit).  State slot of (row, kv_head, split) in
+ *                      both: (row * Hkv + kv_head) * S + split
  *   bucket_rows[B]     rows of every bucket, bucket-major, ascending inside
  * Split s of a row covers pages [page_begin, page_end) and tokens
  * [page_begin * P, min(page_end * P, N_i)).

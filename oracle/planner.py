@@ -24,7 +24,13 @@ Readings where the pages are silent (each listed in the design notes):
 * a bucket's granule is pps_b = max(1, ceil(T_b / S)), ceil(T_b / pps_b) splits;
 * tasks are ordered (row, kv_head, split); buckets by ascending length, rows
   ascending inside a bucket;
-* the no-split path has one task per (row, kv_head) of every non-empty row.
+* the no-split path has one task per (row, kv_head) of every non-empty row;
+* padded power-of-two buckets (the coarse-padding alternative the pages'
+  "Problem statement" contrasts with): rows are grouped by their page count
+  rounded up to a power of two, the bucket's granule is
+  pps_b = max(1, ceil(T_pad / S)) pages of the padded length, and row i keeps
+  its row-local bound -- ceil(T_i / pps_b) non-empty splits; the bucket's
+  other slots are empty (neutral state).  Empty rows form their own bucket.
 """
 from __future__ import annotations
 
@@ -53,7 +59,7 @@ class Plan:
 
 def plan(seq_lens, num_kv_heads: int, num_q_heads: int, head_dim: int, page_size: int,
          splits: int, path: str, elem_bytes: int = 2) -> Plan:
-    """Plan one decode step.  ``path`` is "workqueue", "bucketed" or "nosplit"."""
+    """Plan one decode step.  ``path`` is "workqueue", "bucketed", "padded" or "nosplit"."""
     lens = [int(n) for n in seq_lens]
     b = len(lens)
     hkv = num_kv_heads
@@ -97,6 +103,26 @@ def plan(seq_lens, num_kv_heads: int, num_q_heads: int, head_dim: int, page_size
                         p.tasks.append((i, g, s, s * pps, min((s + 1) * pps, t_b)))
             p.n_state_slots += len(rows) * hkv * splits
             p.n_empty_slots += len(rows) * hkv * (splits - ns)
+        p.row_nsplit = nsplit_row
+        p.n_launches = 2 * len(p.buckets)
+    elif path == "padded":
+        by_pad = {}
+        for i, t in enumerate(pages):
+            pad = 0 if t == 0 else 1 << (t - 1).bit_length()
+            by_pad.setdefault(pad, []).append(i)
+        nsplit_row = [0] * b
+        for pad in sorted(by_pad):
+            pps = max(1, -(-pad // splits))
+            rows = tuple(sorted(by_pad[pad]))
+            p.buckets.append((-1, pad, pps, -(-pad // pps), rows))
+            for i in rows:
+                ns = -(-pages[i] // pps)
+                nsplit_row[i] = ns
+                for g in range(hkv):
+                    for s in range(ns):
+                        p.tasks.append((i, g, s, s * pps, min((s + 1) * pps, pages[i])))
+                p.n_empty_slots += hkv * (splits - ns)
+            p.n_state_slots += len(rows) * hkv * splits
         p.row_nsplit = nsplit_row
         p.n_launches = 2 * len(p.buckets)
     elif path == "nosplit":

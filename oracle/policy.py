@@ -7,7 +7,7 @@ matching rule wins: a rule (b_lo, b_hi, n_lo, n_hi, path, splits) matches when
 b_lo <= B <= b_hi and n_lo <= N_max <= n_hi.  No matching rule -> None.
 
 Parity status: pinned structurally (first match, inclusive bounds, no match)
-in ``tests/test_oracle_policy.py``; the pages' RTX 3060 thresholds do not carry
+in ``tests/test_oracle_planner.py``; the pages' RTX 3060 thresholds do not carry
 over to other hardware, so no threshold value is pinned.
 """
 from __future__ import annotations

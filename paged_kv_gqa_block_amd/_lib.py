@@ -25,12 +25,13 @@ LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE, PKV_ENOSPC, PKV_EHIP = 0, -1, -2, -3, -4, -5, -6
 PKV_F16, PKV_BF16 = 0, 1
-PKV_BUCKETED, PKV_WORKQUEUE, PKV_NOSPLIT = 0, 1, 2
+PKV_BUCKETED, PKV_WORKQUEUE, PKV_NOSPLIT, PKV_PADDED = 0, 1, 2, 3
 PKV_KERNEL_AUTO, PKV_KERNEL_VALU, PKV_KERNEL_MFMA = 0, 1, 2
 PKV_PLAN_MAGIC = 0x31564B50
 PKV_PLAN_HEADER_WORDS = 16
 
-PATH_NAMES = {PKV_BUCKETED: "bucketed", PKV_WORKQUEUE: "workqueue", PKV_NOSPLIT: "nosplit"}
+PATH_NAMES = {PKV_BUCKETED: "bucketed", PKV_WORKQUEUE: "workqueue", PKV_NOSPLIT: "nosplit",
+              PKV_PADDED: "padded"}
 PATH_IDS = {v: k for k, v in PATH_NAMES.items()}
 DTYPE_IDS = {"f16": PKV_F16, "bf16": PKV_BF16}
 KERNEL_IDS = {"auto": PKV_KERNEL_AUTO, "valu": PKV_KERNEL_VALU, "mfma": PKV_KERNEL_MFMA}

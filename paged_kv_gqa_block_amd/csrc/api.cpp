@@ -19,7 +19,7 @@ pkv_status check_plan(const pkv_problem* prob, const void* plan_host, const int3
   if (w[kBatch] != prob->batch || w[kNumKvHeads] != prob->num_kv_heads ||
       w[kWordPageSize] != prob->page_size || w[kWordGroup] != prob->num_q_heads / prob->num_kv_heads)
     return PKV_ESHAPE;
-  if (w[kPath] < PKV_BUCKETED || w[kPath] > PKV_NOSPLIT) return PKV_EINVAL;
+  if (w[kPath] < PKV_BUCKETED || w[kPath] > PKV_PADDED) return PKV_EINVAL;
   *w_out = w;
   return PKV_OK;
 }
@@ -76,7 +76,10 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
     a.num_items = n;
     return launch_split(*prob, kModeNoSplit, prob->kernel, a, n, stream);
   }
-  // BUCKETED: one rectangular rows_b x Hkv x S launch per exact-length bucket.
+  // BUCKETED / PADDED: one rectangular rows_b x Hkv x S launch per bucket.
+  // Rows of a padded bucket differ in length: the kernel takes each row's
+  // length from the plan's row_len array (bucket length word -1).
+  a.row_len = dev + PKV_PLAN_HEADER_WORDS;
   const int32_t* bw = w + w[kOffBuckets];
   for (int k = 0; k < w[kNumBuckets]; ++k) {
     const int32_t* e = bw + kBucketWords * k;
@@ -256,7 +259,7 @@ extern "C" pkv_status pkv_policy(const pkv_policy_table* table, int32_t batch, i
   if (table->n_rules > 0 && !table->rules) return PKV_EINVAL;
   for (int r = 0; r < table->n_rules; ++r) {
     const int32_t* e = table->rules + 6 * r;
-    if (e[4] < PKV_BUCKETED || e[4] > PKV_NOSPLIT || e[5] < 1) return PKV_EINVAL;
+    if (e[4] < PKV_BUCKETED || e[4] > PKV_PADDED || e[5] < 1) return PKV_EINVAL;
   }
   for (int r = 0; r < table->n_rules; ++r) {
     const int32_t* e = table->rules + 6 * r;

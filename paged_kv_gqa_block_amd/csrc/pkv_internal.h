@@ -49,6 +49,7 @@ struct SplitArgs {
   int32_t* device_plan;        // persistent: device-built plan; its task count and the
                                // work counter at word [kTotalWords] are read on the device
   const int32_t* bucket_rows;  // bucket: rows of this bucket
+  const int32_t* row_len;      // bucket: the plan's row lengths N_i
   float* st_m;
   float* st_l;
   float* st_o;
@@ -61,7 +62,8 @@ struct SplitArgs {
   int32_t bucket_pps;
   int32_t bucket_nsplit;
   int32_t bucket_pages;
-  int32_t bucket_len;   // bucket: the rows' common length N_b
+  int32_t bucket_len;   // bucket: the rows' common length N_b, or -1 when
+                        // they differ (padded bucket: lengths from row_len)
   int32_t bucket_row0;  // bucket: its only row when it has one, else -1
   int32_t num_items;    // grid items (tasks, bucket slots or rows * Hkv)
   float scale_log2;   // sm_scale * log2(e)

@@ -1,5 +1,6 @@
-// Host planner: row-local split bounds, the compact workqueue and
-// exact-length buckets, written into the plan buffer described in pkv.h.
+// Host planner: row-local split bounds, the compact workqueue, exact-length
+// and power-of-two padded buckets, written into the plan buffer described in
+// pkv.h.
 //
 // Follows the PersistentKV summary pages, "Methodology / 1. Native
 // block-table decode engine": real per-row lengths set page counts and split
@@ -8,7 +9,10 @@
 // buckets are the alternative it replaces ("Results": launches per step).
 // Where the pages leave the split rule open, the granule is
 // ceil(T_max / S) pages shared by the whole batch for the workqueue, and
-// ceil(T_b / S) per bucket for exact buckets.
+// ceil(T_b / S) per bucket for exact buckets.  Padded buckets group rows by
+// their page count rounded up to a power of two (the coarse padding the
+// pages' "Problem statement" contrasts with); the granule comes from the
+// padded count, the split count of each row from its own pages.
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -20,6 +24,14 @@ namespace pkv {
 namespace {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Smallest power of two >= t (0 for t = 0).
+inline int32_t pow2_ceil(int32_t t) {
+  int32_t p = 1;
+  if (t == 0) return 0;
+  while (p < t) p <<= 1;
+  return p;
+}
 
 }  // namespace
 
@@ -59,7 +71,7 @@ size_t words_upper_bound(const pkv_problem* p, int32_t path, int32_t splits) {
 
 extern "C" size_t pkv_plan_bytes(const pkv_problem* prob, int32_t path, int32_t max_splits) {
   if (check_problem(prob) != PKV_OK) return 0;
-  if (path < PKV_BUCKETED || path > PKV_NOSPLIT) return 0;
+  if (path < PKV_BUCKETED || path > PKV_PADDED) return 0;
   if (max_splits < 1 || max_splits > 65535) return 0;
   return words_upper_bound(prob, path, max_splits) * sizeof(int32_t);
 }
@@ -71,7 +83,7 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
   pkv_status st = check_problem(prob);
   if (st != PKV_OK) return st;
   if (!seq_lens_host || !plan_host) return PKV_EINVAL;
-  if (path < PKV_BUCKETED || path > PKV_NOSPLIT) return PKV_EINVAL;
+  if (path < PKV_BUCKETED || path > PKV_PADDED) return PKV_EINVAL;
   if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
   const int b = prob->batch, hkv = prob->num_kv_heads, psz = prob->page_size;
   const int64_t cap_tokens = int64_t(prob->max_pages_per_row) * psz;
@@ -122,21 +134,24 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
     }
     row_task_off[b] = static_cast<int32_t>(n_tasks);
     n_slots = n_tasks;
-  } else if (path == PKV_BUCKETED) {
+  } else if (path == PKV_BUCKETED || path == PKV_PADDED) {
+    const bool padded = (path == PKV_PADDED);
+    // Bucket key: the exact length, or the padded page count.
+    std::vector<int64_t> key(b);
+    for (int i = 0; i < b; ++i) key[i] = padded ? pow2_ceil(row_pages[i]) : seq_lens_host[i];
     order.resize(b);
     std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int x, int y) { return seq_lens_host[x] < seq_lens_host[y]; });
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return key[x] < key[y]; });
     // Buckets and their rows are appended after the task list once its
     // length is known; collect them first.
     struct Bucket { int32_t len, pages, pps, nsplit, n_rows, first; };
     std::vector<Bucket> bks;
     for (int k = 0; k < b;) {
       int e = k;
-      while (e < b && seq_lens_host[order[e]] == seq_lens_host[order[k]]) ++e;
+      while (e < b && key[order[e]] == key[order[k]]) ++e;
       Bucket bk;
-      bk.len = seq_lens_host[order[k]];
-      bk.pages = row_pages[order[k]];
+      bk.len = padded ? -1 : seq_lens_host[order[k]];
+      bk.pages = padded ? static_cast<int32_t>(key[order[k]]) : row_pages[order[k]];
       bk.pps = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(bk.pages, max_splits)));
       bk.nsplit = static_cast<int32_t>(ceil_div(bk.pages, bk.pps));
       bk.n_rows = e - k;
@@ -144,13 +159,14 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
       bks.push_back(bk);
       for (int j = k; j < e; ++j) {
         const int row = order[j];
-        row_nsplit[row] = bk.nsplit;
+        // Row-local bound: the row's own pages set its split count.
+        row_nsplit[row] = static_cast<int32_t>(ceil_div(row_pages[row], bk.pps));
         for (int g = 0; g < hkv; ++g)
-          for (int s = 0; s < bk.nsplit; ++s)
-            push_task(row, g, s, s * bk.pps, std::min((s + 1) * bk.pps, bk.pages));
+          for (int s = 0; s < row_nsplit[row]; ++s)
+            push_task(row, g, s, s * bk.pps, std::min((s + 1) * bk.pps, row_pages[row]));
+        n_empty += int64_t(hkv) * (max_splits - row_nsplit[row]);
       }
       n_slots += int64_t(bk.n_rows) * hkv * max_splits;
-      n_empty += int64_t(bk.n_rows) * hkv * (max_splits - bk.nsplit);
       k = e;
     }
     n_buckets = static_cast<int32_t>(bks.size());
@@ -189,7 +205,7 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
 
   const int64_t off_buckets = off_tasks + kTaskWords * n_tasks;
   const int64_t off_brows = off_buckets + kBucketWords * int64_t(n_buckets);
-  const int64_t total = off_brows + (path == PKV_BUCKETED ? b : 0);
+  const int64_t total = off_brows + (n_buckets > 0 ? b : 0);
 
   w[kMagic] = PKV_PLAN_MAGIC;
   w[kPath] = path;
@@ -245,7 +261,7 @@ extern "C" pkv_status pkv_plan_get_info(const pkv_problem* prob, const void* pla
   info->pages_per_split = w[kPagesPerSplit];
   if (path == PKV_WORKQUEUE)
     info->n_launches = 1 + (w[kNumTasks] > 0 ? 1 : 0);
-  else if (path == PKV_BUCKETED)
+  else if (path == PKV_BUCKETED || path == PKV_PADDED)
     info->n_launches = 2 * w[kNumBuckets];
   else
     info->n_launches = 1;

@@ -38,10 +38,18 @@ __device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
     t.g = rest % hkv;
     t.row = (a.bucket_row0 >= 0) ? a.bucket_row0 : a.bucket_rows[rest / hkv];
     t.slot = (int64_t(t.row) * hkv + t.g) * a.splits + s;
-    t.empty = s >= a.bucket_nsplit;
+    // Exact bucket: the rows share length, pages and split count.  Padded
+    // bucket: the row's own length bounds its splits (row-local bounds).
+    int n = a.bucket_len, pages = a.bucket_pages, nsplit = a.bucket_nsplit;
+    if (n < 0) {
+      n = a.row_len[t.row];
+      pages = (n + 15) >> 4;
+      nsplit = (pages + a.bucket_pps - 1) / a.bucket_pps;
+    }
+    t.empty = s >= nsplit;
     t.page_begin = s * a.bucket_pps;
-    const int pe = min(t.page_begin + a.bucket_pps, a.bucket_pages);
-    t.tok_end = min(pe * 16, a.bucket_len);
+    const int pe = min(t.page_begin + a.bucket_pps, pages);
+    t.tok_end = min(pe * 16, n);
   } else {
     t.row = item / hkv;
     t.g = item - t.row * hkv;

@@ -83,7 +83,7 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         torch.cuda.synchronize()
         sync_us.append((time.perf_counter() - t) * 1e6)
 
-    n_split = {0: info.n_buckets, 1: 1 if info.n_tasks else 0, 2: 1}[info.path]
+    n_split = {0: info.n_buckets, 1: 1 if info.n_tasks else 0, 2: 1, 3: info.n_buckets}[info.path]
     return {
         "path": path,
         "splits": splits,

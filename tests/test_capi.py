@@ -10,8 +10,8 @@ from oracle.planner import plan as oracle_plan
 from oracle.policy import choose as oracle_choose
 from paged_kv_gqa_block_amd import _lib
 from paged_kv_gqa_block_amd._lib import (PKV_BUCKETED, PKV_EDTYPE, PKV_EINVAL, PKV_ENOSPC,
-                                         PKV_ERANGE, PKV_ESHAPE, PKV_NOSPLIT, PKV_WORKQUEUE,
-                                         PATH_NAMES, PkvError)
+                                         PKV_ERANGE, PKV_ESHAPE, PKV_NOSPLIT, PKV_PADDED,
+                                         PKV_WORKQUEUE, PATH_NAMES, PkvError)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "pkv.h")
@@ -39,7 +39,7 @@ def _plan(prob, lens, path, s):
 
 
 @pytest.mark.parametrize("seed", range(25))
-@pytest.mark.parametrize("path", [PKV_WORKQUEUE, PKV_BUCKETED, PKV_NOSPLIT])
+@pytest.mark.parametrize("path", [PKV_WORKQUEUE, PKV_BUCKETED, PKV_NOSPLIT, PKV_PADDED])
 def test_host_planner_matches_oracle_bit_exactly(seed, path):
     rng = np.random.default_rng(1000 + seed)
     b = int(rng.integers(1, 17))
@@ -64,7 +64,7 @@ def test_host_planner_matches_oracle_bit_exactly(seed, path):
     if path == PKV_WORKQUEUE:
         assert got["row_task_off"] == ref.row_task_off
         assert got["pages_per_split"] == ref.pages_per_split
-    if path == PKV_BUCKETED:
+    if path in (PKV_BUCKETED, PKV_PADDED):
         assert [(bk[0], bk[1], bk[2], bk[3], bk[4]) for bk in got["buckets"]] == [
             (r[0], r[1], r[2], r[3], len(r[4])) for r in ref.buckets]
         rows = []
@@ -106,7 +106,7 @@ def test_policy_matches_oracle(seed):
         b_lo = int(rng.integers(1, 40))
         n_lo = int(rng.integers(0, 20000))
         rules.append((b_lo, b_lo + int(rng.integers(0, 40)), n_lo, n_lo + int(rng.integers(0, 20000)),
-                      int(rng.integers(0, 3)), int(rng.integers(1, 65))))
+                      int(rng.integers(0, 4)), int(rng.integers(1, 65))))
     for _ in range(200):
         b, n = int(rng.integers(1, 80)), int(rng.integers(0, 40000))
         ref = oracle_choose(rules, b, n)
@@ -160,7 +160,7 @@ def test_plan_rejects_bad_lengths_splits_and_small_buffers():
             _lib.pkv_plan(prob, np.array([5, 1], np.int32), PKV_WORKQUEUE, s, buf)
         assert e.value.status == PKV_EINVAL
     with pytest.raises(PkvError) as e:
-        _lib.pkv_plan(prob, np.array([5, 1], np.int32), 3, 4, buf)
+        _lib.pkv_plan(prob, np.array([5, 1], np.int32), 4, 4, buf)
     assert e.value.status == PKV_EINVAL
     need = _lib.pkv_plan_bytes(prob, PKV_WORKQUEUE, 4)
     small = np.zeros(need // 4 - 1, dtype=np.int32)

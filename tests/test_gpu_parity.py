@@ -16,7 +16,7 @@ from tests.parity import check_lse, check_out, oracle_out, say
 pytestmark = pytest.mark.gpu
 
 SEED = traces.HELD_OUT_SEED
-PATHS = ("bucketed", "workqueue", "nosplit")
+PATHS = ("bucketed", "workqueue", "nosplit", "padded")
 KERNELS = ("valu", "mfma")
 
 
@@ -59,7 +59,7 @@ def test_tiny_config_all_paths(path, kernel):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-@pytest.mark.parametrize("path", ("workqueue", "bucketed"))
+@pytest.mark.parametrize("path", ("workqueue", "bucketed", "padded"))
 def test_split_states_match_oracle(path, kernel):
     d = 128 if kernel == "mfma" else 64
     spec = traces.custom_spec(3, 8, 2, d, splits=5)
@@ -82,7 +82,7 @@ def test_split_states_match_oracle(path, kernel):
         on_ref = o[j] / l[j][:, None]
         on_got = go[slot] / gl[slot][:, None]
         assert np.abs(on_got - on_ref).max() <= 1e-4, j
-    if path == "bucketed":
+    if path != "workqueue":
         used = {(row * 2 + g) * 5 + s for (row, g, s, _, _) in plan.tasks}
         for slot in range(plan.n_state_slots):
             if slot not in used:
@@ -118,9 +118,9 @@ def test_merge_kernel_from_oracle_states():
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("name,paths", [
     ("long", ("bucketed", "workqueue", "nosplit")),
-    ("bimodal", ("workqueue", "bucketed", "nosplit")),
-    ("zipf", ("workqueue", "bucketed", "nosplit")),
-    ("uniform", ("workqueue",)),
+    ("bimodal", ("workqueue", "bucketed", "nosplit", "padded")),
+    ("zipf", ("workqueue", "bucketed", "nosplit", "padded")),
+    ("uniform", ("workqueue", "bucketed", "nosplit", "padded")),
 ])
 def test_full_size_configs(name, paths, kernel):
     w = traces.generate(traces.get_spec(name), SEED)
@@ -140,7 +140,7 @@ def test_policy_sweep_slice_bf16(batch, kernel):
     w = traces.generate(traces.get_spec(f"policy_b{batch}"), SEED)
     say(f"[policy_b{batch}] kernel={kernel}")
     ref_out, ref_lse = oracle_out(w)
-    for path, s in (("workqueue", 32), ("bucketed", 16), ("nosplit", 1)):
+    for path, s in (("workqueue", 32), ("bucketed", 16), ("nosplit", 1), ("padded", 16)):
         step, _ = _run(w, path, s, kernel)
         check_out(step.out, ref_out, "bf16", label=f"policy_b{batch}/{path}")
         check_lse(step.lse, ref_lse, label=f"policy_b{batch}/{path}")
@@ -160,7 +160,7 @@ def test_edge_lengths_shapes_and_dtypes(d, hq, hkv, dtype, kernel):
     say(f"[edge] d={d} hq={hq} hkv={hkv} {dtype} kernel={kernel}")
     ref_out, ref_lse = oracle_out(w)
     for path, s in (("workqueue", 3), ("workqueue", 40), ("bucketed", 3), ("bucketed", 40),
-                    ("nosplit", 1)):
+                    ("nosplit", 1), ("padded", 3), ("padded", 40)):
         step, _ = _run(w, path, s, kernel)
         check_out(step.out, ref_out, dtype, label=f"edge/{path}/S={s}")
         check_lse(step.lse, ref_lse, label=f"edge/{path}/S={s}")
@@ -215,7 +215,8 @@ def test_policy_sweep_large_batches_sampled_rows(batch):
     ref_out, ref_lse = oracle_out(w, rows=rows)
     rules = engine.load_policy_table()
     chosen = engine.choose(rules, batch, int(lens.max()))
-    for path, s in dict.fromkeys([chosen, ("workqueue", 32), ("bucketed", 32), ("nosplit", 1)]):
+    for path, s in dict.fromkeys([chosen, ("workqueue", 32), ("bucketed", 32), ("nosplit", 1),
+                                  ("padded", 32)]):
         step, _ = _run(w, path, s, "auto")
         check_out(step.out, ref_out, "bf16", rows=rows, label=f"policy_b{batch}/{path}:{s}")
         check_lse(step.lse, ref_lse, rows=rows, label=f"policy_b{batch}/{path}:{s}")

@@ -32,7 +32,7 @@ def _check_partition(p, lens, hkv, page_size):
 
 
 @pytest.mark.parametrize("seed", range(20))
-@pytest.mark.parametrize("path", ["workqueue", "bucketed", "nosplit"])
+@pytest.mark.parametrize("path", ["workqueue", "bucketed", "nosplit", "padded"])
 def test_plan_partitions_rows(seed, path):
     rng = np.random.default_rng(seed)
     b = int(rng.integers(1, 9))
@@ -79,6 +79,51 @@ def test_bucketed_closed_forms():
     assert p.n_state_slots == 4 * 2 * 4
     assert p.n_empty_slots == 1 * 2 * 4 + 1 * 2 * 2
     assert p.row_nsplit == [4, 2, 4, 0]
+
+
+def test_padded_closed_forms():
+    # T = 19, 2, 19, 0, 5, 32 pages -> padded 32, 2, 32, 0, 8, 32.
+    lens = [300, 17, 300, 0, 65, 512]
+    p = plan(lens, 2, 4, 64, 16, 4, "padded")
+    assert [bk[1] for bk in p.buckets] == [0, 2, 8, 32]
+    assert p.buckets[0] == (-1, 0, 1, 0, (3,))
+    assert p.buckets[1] == (-1, 2, 1, 2, (1,))        # pps = max(1, ceil(2/4)) = 1
+    assert p.buckets[2] == (-1, 8, 2, 4, (4,))        # T=5 padded to 8: pps 2, row gets 3
+    assert p.buckets[3] == (-1, 32, 8, 4, (0, 2, 5))  # pps 8: T=19 -> 3 splits, T=32 -> 4
+    assert p.row_nsplit == [3, 2, 3, 0, 3, 4]
+    assert p.n_launches == 8
+    assert p.n_state_slots == 6 * 2 * 4
+    # Row-local bounds: slots past each row's own split count are empty.
+    assert p.n_empty_slots == 2 * sum(4 - ns for ns in p.row_nsplit)
+    # The last split of a row stops at its real last page, not the padded one.
+    assert (0, 1, 2, 16, 19) in p.tasks and (4, 0, 2, 4, 5) in p.tasks
+    assert len(p.tasks) == 2 * sum(p.row_nsplit)
+
+
+def test_padded_equals_bucketed_on_power_of_two_pages():
+    """Rows whose page counts are distinct powers of two: padding is the identity."""
+    lens = [16 * 1, 16 * 64, 16 * 8, 16 * 2048, 0]
+    for s in [1, 3, 32]:
+        a = plan(lens, 8, 32, 128, 16, s, "padded")
+        b = plan(lens, 8, 32, 128, 16, s, "bucketed")
+        assert a.tasks == b.tasks and a.row_nsplit == b.row_nsplit
+        assert a.n_launches == b.n_launches and a.n_empty_slots == b.n_empty_slots
+        assert [bk[1:] for bk in a.buckets] == [bk[1:] for bk in b.buckets]
+
+
+def test_padded_brute_force_buckets():
+    """Bucket of each row is the least power of two >= T_i; launches 2 x #distinct."""
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        lens = rng.integers(0, 5000, size=int(rng.integers(1, 12)))
+        p = plan(lens, 1, 1, 64, 16, 8, "padded")
+        want = {}
+        for i, n in enumerate(lens):
+            t = pages_of(n, 16)
+            pad = next(q for q in [0] + [1 << k for k in range(20)] if q >= t)
+            want.setdefault(pad, []).append(i)
+        assert [(bk[1], bk[4]) for bk in p.buckets] == [(k, tuple(v)) for k, v in sorted(want.items())]
+        assert p.n_launches == 2 * len(want)
 
 
 def test_single_row_bucketed_equals_workqueue():
