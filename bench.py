@@ -1,7 +1,7 @@
 """Decode-attention benchmark: µs per decode step and achieved HBM GB/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
-                    [--path bucketed|workqueue|nosplit|policy] [--kernel auto|valu|mfma]
+                    [--path bucketed|workqueue|nosplit|padded|policy] [--kernel auto|valu|mfma]
 
 One step is the engine's device work for one decode step of one layer: the
 split kernel launch(es) and the merge launch(es) (or the single no-split
@@ -151,7 +151,8 @@ def run_all(args) -> int:
         engine.validate_inputs(wd)
         views = timing.pool_copies(wd, args.copies_gib, max_copies=8)
         pol = engine.choose(rules, spec.batch, int(lens.max()))
-        cands = [("bucketed", spec.splits), ("workqueue", spec.splits), ("nosplit", 1)]
+        cands = [("bucketed", spec.splits), ("workqueue", spec.splits), ("nosplit", 1),
+                 ("padded", spec.splits)]
         if pol not in cands:
             cands.append(pol)
         cpu = None if args.no_cpu_baseline else cpu_baseline(w, min(args.cpu_budget_s, 5.0))

@@ -6,16 +6,18 @@ The PersistentKV summary pages ("2. Calibrated adaptive policy"; "Results":
 thresholds fixed on calibration seed 20260622, results on held-out seed
 20260623) pick the execution path from the batch size B and the longest
 context N_max with hand-calibrated thresholds.  Here the thresholds are
-measured on this GPU.  Every candidate (bucketed or workqueue with a split
-cap of 8/16/32/64, or the single-pass no-split kernel) is timed on the
+measured on this GPU.  Every candidate (exact buckets, the workqueue or
+power-of-two padded buckets with a split cap of 8/16/32/64, or the
+single-pass no-split kernel) is timed on the
 calibration seed for every batch size of the sweep (64/8 heads, d=128, bf16)
 at a grid of longest lengths H: one row of length H for B = 1 (a single row's
 work is set by its length alone), and B rows drawn like the sweep families
-capped at H for larger B (U[64,H] for H <= 2048, U[1024,H] above).  The
+capped at H for larger B (U[64,H] for H <= 2048, U[1024,H] above), with the
+candidates' timed repeats interleaved (median of 7).  The
 fastest candidate becomes the rule of its (B range, N_max interval) cell,
 with interval boundaries at the geometric midpoints between grid values.  The table is then
-checked on the held-out seed on the two families against the three fixed
-single paths (bucketed S=32, workqueue S=32, no-split): per batch size the
+checked on the held-out seed on the two families against the four fixed
+single paths (bucketed S=32, workqueue S=32, no-split, padded S=32): per batch size the
 policy's time must be within the noise band of the best one.
 """
 from __future__ import annotations
@@ -32,8 +34,9 @@ import torch
 from . import engine, timing, traces
 
 CANDIDATES = ([("bucketed", s) for s in (8, 16, 32, 64)] +
-              [("workqueue", s) for s in (8, 16, 32, 64)] + [("nosplit", 1)])
-SINGLE_PATHS = (("bucketed", 32), ("workqueue", 32), ("nosplit", 1))
+              [("workqueue", s) for s in (8, 16, 32, 64)] +
+              [("padded", s) for s in (8, 16, 32, 64)] + [("nosplit", 1)])
+SINGLE_PATHS = (("bucketed", 32), ("workqueue", 32), ("nosplit", 1), ("padded", 32))
 SINGLE_ROW_LENGTHS = (128, 256, 512, 768, 1024, 1536, 2048, 3072, 4096, 8192, 16384, 32768)
 CAPS = (256, 512, 1024, 1536, 2048, 4096, 8192, 16384, 32768)
 FAMILIES = (("short", "policy_short_b{}"), ("long", "policy_b{}"))
@@ -67,11 +70,11 @@ def measure(spec: traces.WorkloadSpec, seed: int, configs, steps: int, warmup: i
     wd = engine.to_device(w)
     engine.validate_inputs(wd)
     views = timing.pool_copies(wd, 1.0, max_copies=8)
+    times = timing.time_paths_interleaved(w, views, configs, "auto", steps, warmup, repeats=7)
     out = {}
     for path, s in configs:
-        r = timing.time_path(w, views, path, s, "auto", steps, warmup, sync_reps=0, repeats=5)
-        out[f"{path}:{s}"] = round(r["step_us"], 2)
-        log(f"  {name} seed={seed} {path:9s} S={s:2d}: {r['step_us']:9.2f} us/step")
+        out[f"{path}:{s}"] = round(times[f"{path}:{s}"], 2)
+        log(f"  {name} seed={seed} {path:9s} S={s:2d}: {out[f'{path}:{s}']:9.2f} us/step")
     n_max = int(w["seq_lens"].max())
     del views, wd, w
     torch.cuda.empty_cache()

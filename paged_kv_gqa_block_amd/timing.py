@@ -98,6 +98,41 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
     }
 
 
+def time_paths_interleaved(w: dict, views, configs, kernel: str = "auto", steps: int = 30,
+                           warmup: int = 5, repeats: int = 7) -> dict:
+    """Step time of several (path, split cap) configurations of one workload.
+
+    The timed loops alternate between the configurations (repeat r of every
+    configuration before repeat r + 1 of any), so a drift of the GPU's clock
+    during the measurement moves all of them alike; each result is the median
+    over its repeats.  Returns {"path:splits": step_us}.
+    """
+    prob = engine.problem_from_workload(w, kernel)
+    stream = torch.cuda.current_stream()
+    n = len(views)
+    steps_by = {}
+    for path, s in configs:
+        st = engine.DecodeStep(prob, path, s)
+        st.plan(views[0]["seq_lens_host"], stream=stream)
+        for i in range(warmup):
+            st.run(views[i % n], stream)
+        steps_by[f"{path}:{s}"] = st
+    torch.cuda.synchronize()
+    runs = {k: [] for k in steps_by}
+    k0 = 0
+    for _rep in range(repeats):
+        for key, st in steps_by.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                st.run(views[(k0 + i) % n], stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            runs[key].append(1e3 * e0.elapsed_time(e1) / steps)
+            k0 += steps
+    return {k: statistics.median(v) for k, v in runs.items()}
+
+
 def time_device_path(w: dict, views, splits: int, steps: int = 50, warmup: int = 10,
                      sync_reps: int = 20, repeats: int = 5, graph: bool = False) -> dict:
     """Times the device-planned workqueue step (plan + persistent split + merge
