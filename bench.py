@@ -13,8 +13,10 @@ pools (as consecutive layers of a model would), with enough copies to exceed
 
 Printed JSON line: value = real-KV bytes (sum N_i * Hkv * d * 2 * 2) divided by
 the device step time measured with HIP events on the launch stream.  The
-roofline object reports the split kernel alone; cpu_baseline times the fp64
-CPU oracle on the same generated inputs.
+roofline object reports the split kernel alone, against the 8 TB/s HBM peak
+and, beside it, against a read-only probe kernel that streams exactly the
+same pages (the rate this access pattern reaches on the device);
+cpu_baseline times the fp64 CPU oracle on the same generated inputs.
 """
 from __future__ import annotations
 
@@ -156,6 +158,12 @@ def run_all(args) -> int:
         if pol not in cands:
             cands.append(pol)
         cpu = None if args.no_cpu_baseline else cpu_baseline(w, min(args.cpu_budget_s, 5.0))
+        pr = timing.time_read_probe(w, views, "workqueue", spec.splits, args.steps, args.warmup)
+        print(json.dumps({"workload": describe(spec, "read-only probe", spec.splits, lens),
+                          "config": name, "path": "read_only_probe", "splits": spec.splits,
+                          "us_per_step": round(pr["us_per_launch"], 2),
+                          "GB/s": round(pr["GB/s"], 1),
+                          "pct_of_peak": round(100 * pr["GB/s"] / HBM_PEAK_GBS, 1)}), flush=True)
         if spec.head_dim == 128:
             for graph in (False, True):
                 r = timing.time_device_path(w, views, spec.splits, args.steps, args.warmup,
@@ -258,6 +266,13 @@ def main(argv=None):
                      "launch_us": round(split_launch_us, 2),
                      "algorithmic_bytes_per_launch": kv // max(1, r["n_split_launches"])},
     }
+    if r["n_split_launches"] == 1:
+        # The same tasks' pages streamed by a read-only kernel: the rate this
+        # access pattern reaches on the device (the split kernel's ceiling).
+        pr = timing.time_read_probe(w, views, path, splits, args.steps, args.warmup)
+        line["roofline"]["read_only_probe"] = {
+            "GB/s": round(pr["GB/s"], 1), "launch_us": round(pr["us_per_launch"], 2),
+            "achieved_over_probe": round(split_gbs / pr["GB/s"], 4)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
     print(json.dumps(line), flush=True)

@@ -1,4 +1,5 @@
-"""Compile libpkv.so (host planner + HIP kernels for gfx950) in-tree.
+"""Compile libpkv.so (host planner + HIP kernels for gfx950) and the
+read-bandwidth probe libpkv_probe.so (a measurement tool) in-tree.
 
     python -m paged_kv_gqa_block_amd.build
 
@@ -18,12 +19,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libpkv.so")
+PROBE_LIB_PATH = os.path.join(PKG, "libpkv_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [
     "planner.cpp", "api.cpp", "merge.hip", "split_valu.hip", "split_mfma.hip", "planner_device.hip",
     "append.hip",
 ]
+PROBE_SOURCES = ["read_probe.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", f"-I{INCLUDE}", f"-I{CSRC}",
@@ -44,19 +47,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_LIB_PATH}")
     return LIB_PATH
 
 

@@ -1,0 +1,70 @@
+// Read-only bandwidth probe (libpkv_probe.so): streams every page chunk the
+// split kernel would read for a plan's tasks, with nothing else in the loop.
+// Interface and purpose in include/pkv_probe.h.
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "pkv.h"
+#include "pkv_probe.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kDepth = 2;  // pages of loads a wave keeps in flight
+
+// One workgroup per task; wave w reads the task's pages w, w + 4, ... two at a
+// time.  U = 16-byte loads per lane per page chunk (4 for d = 128, 2 for 64).
+template <int U>
+__global__ __launch_bounds__(kWaves * 64) void probe_read_kernel(
+    const uint4* __restrict__ k, const uint4* __restrict__ v, const int32_t* __restrict__ bt,
+    int max_pages, int hkv, const int4* __restrict__ tasks, uint32_t* sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int4 task = tasks[blockIdx.x];
+  const int row = task.x, g = task.y >> 16;
+  const int pb = task.z, pe = (task.w + 15) >> 4;
+  const int32_t* bt_row = bt + int64_t(row) * max_pages;
+  uint32_t acc = 0;
+  for (int p0 = pb + wave * kDepth; p0 < pe; p0 += kWaves * kDepth) {
+    uint4 buf[kDepth][2 * U];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int p = min(p0 + d, pe - 1);
+      const int64_t base = (int64_t(bt_row[p]) * hkv + g) * (64 * U);
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        buf[d][i] = k[base + i * 64 + lane];
+        buf[d][U + i] = v[base + i * 64 + lane];
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+      for (int i = 0; i < 2 * U; ++i) acc += buf[d][i].x ^ buf[d][i].y ^ buf[d][i].z ^ buf[d][i].w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // keeps the loads; practically never true
+}
+
+}  // namespace
+
+extern "C" int pkv_probe_read(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                              int32_t max_pages_per_row, int32_t num_kv_heads, int32_t head_dim,
+                              const void* plan_host, const void* plan_dev, uint32_t* sink,
+                              hipStream_t stream) {
+  if (!k_pool || !v_pool || !block_table || !plan_host || !plan_dev || !sink) return -1;
+  if ((head_dim != 64 && head_dim != 128) || num_kv_heads < 1 || max_pages_per_row < 1) return -1;
+  const int32_t* w = static_cast<const int32_t*>(plan_host);
+  if (w[0] != PKV_PLAN_MAGIC || w[3] != num_kv_heads || w[14] != 16) return -1;
+  const int n_tasks = w[6];
+  if (n_tasks == 0) return 0;
+  const int4* tasks = reinterpret_cast<const int4*>(static_cast<const int32_t*>(plan_dev) + w[10]);
+  const uint4* k = static_cast<const uint4*>(k_pool);
+  const uint4* v = static_cast<const uint4*>(v_pool);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(probe_read_kernel<4>, dim3(n_tasks), dim3(kWaves * 64), 0, stream, k, v,
+                       block_table, max_pages_per_row, num_kv_heads, tasks, sink);
+  else
+    hipLaunchKernelGGL(probe_read_kernel<2>, dim3(n_tasks), dim3(kWaves * 64), 0, stream, k, v,
+                       block_table, max_pages_per_row, num_kv_heads, tasks, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}

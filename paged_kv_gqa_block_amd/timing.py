@@ -133,6 +133,36 @@ def time_paths_interleaved(w: dict, views, configs, kernel: str = "auto", steps:
     return {k: statistics.median(v) for k, v in runs.items()}
 
 
+def time_read_probe(w: dict, views, path: str, splits: int, steps: int = 50,
+                    warmup: int = 10, repeats: int = 5) -> dict:
+    """Read-only probe over the pages of one plan's tasks (libpkv_probe.so):
+    the HBM rate of the split kernel's access pattern with no compute.
+    Returns the median µs per probe launch and the real-KV GB/s it implies."""
+    from . import probe
+
+    prob = engine.problem_from_workload(w, "auto")
+    step = engine.DecodeStep(prob, path, splits)
+    stream = torch.cuda.current_stream()
+    info = step.plan(views[0]["seq_lens_host"], stream=stream)
+    sink = torch.zeros(max(1, info.n_tasks), dtype=torch.int32, device="cuda")
+    n = len(views)
+    for i in range(warmup):
+        probe.probe_read(views[i % n], step, sink, stream)
+    torch.cuda.synchronize()
+    runs = []
+    for rep in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            probe.probe_read(views[(warmup + rep * steps + i) % n], step, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        runs.append(1e3 * e0.elapsed_time(e1) / steps)
+    us = statistics.median(runs)
+    return {"us_per_launch": us, "GB/s": info.kv_bytes / (us * 1e-6) / 1e9,
+            "n_tasks": info.n_tasks}
+
+
 def time_device_path(w: dict, views, splits: int, steps: int = 50, warmup: int = 10,
                      sync_reps: int = 20, repeats: int = 5, graph: bool = False) -> dict:
     """Times the device-planned workqueue step (plan + persistent split + merge

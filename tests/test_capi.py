@@ -245,3 +245,13 @@ def test_append_validates_before_launch():
     with pytest.raises(PkvError) as e:
         _lib.pkv_append_kv(bad, fake, fake, fake, fake, fake, fake)
     assert e.value.status == PKV_ESHAPE
+
+
+def test_probe_library_exports_its_header():
+    from paged_kv_gqa_block_amd import probe
+
+    with open(os.path.join(os.path.dirname(HEADER), "pkv_probe.h")) as f:
+        declared = set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(pkv_\w+)\s*\(", f.read(), flags=re.M))
+    assert declared == set(probe.EXPORTED)
+    for name in declared:
+        assert hasattr(probe.LIB, name), name
