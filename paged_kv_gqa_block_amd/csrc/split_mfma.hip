@@ -317,8 +317,12 @@ __device__ __forceinline__ void mfma_task(const SplitArgs& a, Task tk, MfmaShare
 // Grid modes: one workgroup per workqueue task / bucket slot / (row, KV head);
 // or persistent: a fixed grid claiming tasks of a device-built workqueue whose
 // task count is read from the plan on the device.
+// With one page in flight per wave (PF = 1) the kernel fits in 168 registers
+// per lane without spilling, so three waves share each SIMD (three
+// workgroups per CU) instead of the two the compiler would otherwise pick.
 template <int GP, bool BF16, int NW, int PF, int MODE>
-__global__ __launch_bounds__(NW * 64) void split_mfma_kernel(SplitArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 3 : 1, 8)))
+void split_mfma_kernel(SplitArgs a) {
   __shared__ MfmaShared<GP, NW> sh;
   if constexpr (MODE == kModePersistent) {
     // Workgroups claim tasks from a device-scope counter (zeroed by the
@@ -366,10 +370,12 @@ pkv_status launch_mfma_modes(int mode, const SplitArgs& a, int grid, hipStream_t
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-// 4 waves per workgroup with one page in flight per wave (140 VGPRs): up to
-// three workgroups share a CU, so one task's start-up overlaps another's
-// streaming.  Measured on MI355X against 8 waves and/or two pages in flight:
-// equal on one long row, 5-8 % faster on batched workloads.
+// 4 waves per workgroup with one page in flight per wave (139 registers,
+// three waves per SIMD): three workgroups share a CU, so one task's start-up
+// overlaps another's streaming.  Measured on MI355X against 8 waves and/or
+// two pages in flight: equal on one long row, 5-8 % faster on batched
+// workloads; three resident workgroups instead of two: 0.5-2 % faster on
+// every workload.
 template <bool BF16>
 pkv_status launch_mfma_g(int gp, int mode, const SplitArgs& a, int grid, hipStream_t s) {
   switch (gp) {
