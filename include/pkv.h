@@ -146,6 +146,7 @@ typedef struct pkv_policy_table {
  *   [16+2B ..]         row_nsplit[B]
  *   [16+3B ..]         row_task_off[B+1] (first task of each row in task
  *                      order; entry B = n_tasks)
+ *   (0 to 3 zero words, so that the task list starts 16-byte aligned)
  *   tasks[n_tasks][4]  { row, (kv_head << 16) | split, page_begin, token_end }
  *                      with token_end = min(page_end * P, N_row) (so
  *                      page_end = ceil(token_end / P)), starting at word

@@ -99,6 +99,8 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
   int32_t* row_task_off = row_nsplit + b;
   int64_t off_tasks = (PKV_PLAN_HEADER_WORDS + 4 * int64_t(b) + 1 + 3) & ~int64_t(3);
   int32_t* tasks = w + off_tasks;
+  // Alignment words between row_task_off and the task list.
+  for (int64_t i = PKV_PLAN_HEADER_WORDS + 4 * int64_t(b) + 1; i < off_tasks; ++i) w[i] = 0;
 
   int32_t t_max = 0;
   for (int i = 0; i < b; ++i) {

@@ -131,6 +131,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_workqueue_kernel(
     tasks[j] = make_int4(row, (g << 16) | sp, pb, min(pe * page_size, n));
   }
   if (tid == 0) {
+    // Alignment words between row_task_off and the task list.
+    for (int i = PKV_PLAN_HEADER_WORDS + 4 * batch + 1; i < off_tasks; ++i) plan[i] = 0;
     plan[kMagic] = PKV_PLAN_MAGIC;
     plan[kPath] = PKV_WORKQUEUE;
     plan[kBatch] = batch;

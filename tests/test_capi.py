@@ -218,6 +218,10 @@ def test_device_plan_entry_points_validate_before_launch():
     with pytest.raises(PkvError) as e:
         _lib.pkv_plan_device(prob, fake, 0, fake, need)
     assert e.value.status == PKV_EINVAL
+    big = _prob(16385)  # one row past the device planner's limit
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_plan_device(big, fake, 8, fake, _lib.pkv_plan_bytes(big, PKV_WORKQUEUE, 8))
+    assert e.value.status == PKV_ERANGE
     with pytest.raises(PkvError) as e:  # d = 64 has no persistent kernel
         _lib.pkv_decode_device(_prob(2, d=64), fake, 8, fake, fake, fake, fake, fake, fake, fake)
     assert e.value.status == PKV_ESHAPE

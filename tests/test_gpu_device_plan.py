@@ -45,6 +45,27 @@ def test_device_plan_equals_host_plan(seed):
     assert int(step.bad_rows.item()) == 0
 
 
+def test_device_plan_at_the_batch_limit():
+    """16384 rows (the device planner's maximum), ~2 M tasks: word for word."""
+    rng = np.random.default_rng(99)
+    b, hkv, s = 16384, 8, 32
+    lens = rng.integers(0, 4096, size=b, endpoint=True).astype(np.int32)
+    lens[rng.random(b) < 0.1] = 0
+    say(f"[device plan] B={b} Hkv={hkv} S={s}")
+    prob = _lib.make_problem(b, hkv * 4, hkv, 128, 16, 1 << 20, 256)
+    host = _host_plan(prob, lens, s)
+    plan_dev = torch.full((host.size,), -7, dtype=torch.int32, device="cuda")  # every word used must be written
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _lib.pkv_plan_device(prob, torch.from_numpy(lens).cuda(), s, plan_dev, bad_rows_dev=bad)
+    torch.cuda.synchronize()
+    total = int(host[13])
+    dev = plan_dev.cpu().numpy()
+    np.testing.assert_array_equal(dev[:total], host[:total])
+    assert int(bad.item()) == 0
+    assert int(host[6]) > 1_000_000
+    assert int(dev[total]) == 0  # work counter zeroed
+
+
 def _device_run(w, splits):
     wd = engine.to_device(w)
     engine.validate_inputs(wd)
