@@ -240,11 +240,11 @@ pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void*
  * [0, max_pages_per_row * P] is planned as an empty row, and the number of
  * such rows is written to *bad_rows_dev when it is not NULL.
  *
- * pkv_decode_device runs the split kernel as a persistent grid (two
- * workgroups per compute unit, at most B * Hkv * max_splits) whose workgroups
- * claim tasks of the device-built list through a work counter kept in plan
- * word [total_words] (just past the task list; pkv_plan_bytes leaves room for
- * it).  pkv_plan_device zeroes the counter and pkv_merge_device resets it, so
+ * pkv_decode_device runs the split kernel as a persistent grid (as many
+ * workgroups as fit on the device at once, at most B * Hkv * max_splits):
+ * workgroup w runs task w, and further tasks are claimed through a work
+ * counter kept in plan word [total_words] (just past the task list;
+ * pkv_plan_bytes leaves room for it).  pkv_plan_device zeroes the counter and pkv_merge_device resets it, so
  * every pkv_decode_device must follow a pkv_plan_device or a pkv_merge_device
  * on the same plan; calls that overlap on one plan race.  It writes st_m, st_l, st_o exactly as pkv_decode does for the
  * WORKQUEUE path (slot = task index); the state buffers must hold

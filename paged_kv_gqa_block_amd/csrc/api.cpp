@@ -200,9 +200,11 @@ extern "C" pkv_status pkv_decode_device(const pkv_problem* prob, const void* pla
   // located from the plan header on the device.
   a.device_plan = const_cast<int32_t*>(plan);
   a.bucket_row0 = -1;
-  // Two resident workgroups per CU, never more than the largest task count.
+  // As many workgroups as can be resident (three per CU for G <= 8, two for
+  // larger groups), never more than the largest task count.
+  const int per_cu = (prob->num_q_heads / prob->num_kv_heads <= 8) ? 3 : 2;
   const int64_t upper = int64_t(prob->batch) * prob->num_kv_heads * max_splits;
-  const int grid = static_cast<int>(std::min<int64_t>(upper, 2 * int64_t(cus)));
+  const int grid = static_cast<int>(std::min<int64_t>(upper, int64_t(per_cu) * cus));
   a.num_items = grid;
   return launch_split(*prob, kModePersistent, prob->kernel, a, grid, stream);
 }

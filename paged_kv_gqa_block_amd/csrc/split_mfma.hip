@@ -325,20 +325,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PF == 1
 void split_mfma_kernel(SplitArgs a) {
   __shared__ MfmaShared<GP, NW> sh;
   if constexpr (MODE == kModePersistent) {
-    // Workgroups claim tasks from a device-scope counter (zeroed by the
-    // device planner and reset by the device merge), so tasks go to whichever
-    // workgroups are running; every workgroup exits once the counter passes
-    // the task count, and none ever waits on another.
+    // Workgroup w first runs task w; further tasks (grid + k for the k-th
+    // claim) come from a device-scope counter, zeroed by the device planner
+    // and reset by the device merge, so they go to whichever workgroups are
+    // running.  A workgroup exits once its task index passes the task count
+    // (or at once after its first task when the grid covers every task), and
+    // none ever waits on another.
     __shared__ int s_task;
     const int n_tasks = a.device_plan[kNumTasks];
+    const int grid = static_cast<int>(gridDim.x);
     int32_t* counter = a.device_plan + a.device_plan[kTotalWords];
-    for (;;) {
-      if (threadIdx.x == 0) s_task = atomicAdd(counter, 1);
-      __syncthreads();
-      const int t = s_task;
-      if (t >= n_tasks) break;
+    int t = static_cast<int>(blockIdx.x);
+    while (t < n_tasks) {
       mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, decode_task<kModeWorkqueue>(a, t), sh);
+      if (n_tasks <= grid) break;
       __syncthreads();  // LDS (and s_task) are reused by the next task
+      if (threadIdx.x == 0) s_task = grid + atomicAdd(counter, 1);
+      __syncthreads();
+      t = s_task;
     }
   } else {
     const Task tk = decode_task<MODE>(a, blockIdx.x);
