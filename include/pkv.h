@@ -18,7 +18,8 @@
  *     exit early;
  *   - Compact workqueue: a 1-D grid over only the non-empty
  *     (row, kv-head, split) intervals, instead of one launch pair per exact
- *     length bucket.
+ *     length bucket (or per padded length bucket, the coarse alternative of
+ *     the "Problem statement" section).
  * Section "2. Calibrated adaptive policy" picks the execution path from the
  * batch size B and the longest context N_max with calibrated thresholds.
  *
@@ -184,6 +185,11 @@ size_t pkv_plan_bytes(const pkv_problem* prob, int32_t path, int32_t max_splits)
  *   BUCKETED:  rows grouped by exact length; bucket b uses
  *              pps_b = max(1, ceil(T_b / S)) and ceil(T_b / pps_b) splits;
  *              its grid has rows_b * Hkv * S slots, the rest neutral.
+ *   PADDED:    rows grouped by T_i rounded up to a power of two (0 stays 0);
+ *              bucket b uses pps_b = max(1, ceil(T_pad / S)) pages; row i
+ *              gets ceil(T_i / pps_b) splits (row-local bound), the last
+ *              ending at T_i; its grid has rows_b * Hkv * S slots, the rest
+ *              neutral.
  *   NOSPLIT:   one task per (row, kv head) of every non-empty row.
  * Errors: PKV_EINVAL (null pointer, max_splits < 1 or > 65535, bad path),
  * PKV_ESHAPE (problem shape), PKV_ERANGE (N_i < 0 or N_i > max_pages_per_row*P),
@@ -202,7 +208,7 @@ pkv_status pkv_plan_get_info(const pkv_problem* prob, const void* plan_host,
  * Split decode (the engine's first kernel, or the whole step for NOSPLIT).
  * plan_host is read for launch shapes; plan_dev (the device copy of the same
  * plan, already enqueued on `stream`) is read by the kernels.
- *   WORKQUEUE / BUCKETED: writes st_m, st_l, st_o for all n_state_slots
+ *   WORKQUEUE / BUCKETED / PADDED: writes st_m, st_l, st_o for all n_state_slots
  *     slots (neutral (-inf, 0, 0) for empty slots); out and lse are unused.
  *   NOSPLIT: writes out (and lse when not NULL) for every row; st_* unused
  *     and may be NULL.  Rows with N_i = 0 get out = 0, lse = -inf.
@@ -221,7 +227,8 @@ pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host, const void
  * row's partial states exactly: M = max_s m_s, w_s = exp(m_s - M),
  * L = sum_s w_s l_s, out = sum_s w_s o_s / L rounded to nearest-even into the
  * problem dtype, lse = M + ln L.  All-neutral rows give out = 0, lse = -inf.
- * WORKQUEUE: one launch; BUCKETED: one launch per bucket; NOSPLIT: no-op.
+ * WORKQUEUE: one launch; BUCKETED / PADDED: one launch per bucket;
+ * NOSPLIT: no-op.
  * lse may be NULL.  Errors as pkv_decode.
  */
 pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void* plan_dev,
