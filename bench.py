@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # Counter-based HBM traffic of the split kernel per workload (rocprofv3
 # FETCH_SIZE + WRITE_SIZE runs, scaled against a copy kernel); reported only
 # while the kernel sources still hash to the value recorded with it.
-TRAFFIC_PROFILES = {"long": "profiles/split_mfma_long_b1_n32768_traffic.txt"}
+TRAFFIC_PROFILES = {"long": "profiles/split_mfma_long_b1_n32768_traffic.txt",
+                    "bimodal": "profiles/split_mfma_bimodal_b8_traffic.txt"}
 KERNEL_SOURCES = ("split_mfma.hip", "split_common.h", "device_common.h", "pkv_internal.h")
 DEFAULT_PATH = {"tiny": "workqueue", "long": "bucketed", "bimodal": "workqueue",
                 "zipf": "workqueue", "uniform": "workqueue"}
@@ -77,10 +78,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(config: str, kernel_used: str):
-    """Traffic bytes per split launch from profiles/, or None if absent or stale."""
+def recorded_traffic(config: str, kernel_used: str, path: str, splits: int, seed: int):
+    """Traffic bytes per split launch from profiles/, or None if absent, stale or
+    taken in another launch configuration (the profiles use the workload's
+    default path and split cap, seed 20260623)."""
+    from paged_kv_gqa_block_amd import traces
+
     rel = TRAFFIC_PROFILES.get(config)
     if rel is None or kernel_used != "mfma":
+        return None
+    if (path != DEFAULT_PATH.get(config) or splits != traces.get_spec(config).splits
+            or seed != traces.HELD_OUT_SEED):
         return None
     try:
         with open(os.path.join(ROOT, rel)) as f:
@@ -261,7 +269,7 @@ def main(argv=None):
                    "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.config, kernel_used),
+                     "traffic": recorded_traffic(args.config, kernel_used, path, splits, seed),
                      "kernel": f"split decode ({kernel_used})",
                      "launch_us": round(split_launch_us, 2),
                      "algorithmic_bytes_per_launch": kv // max(1, r["n_split_launches"])},
