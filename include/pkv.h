@@ -92,7 +92,10 @@ enum {
                         write neutral state and read no KV)                */
 };
 
-/* Split-kernel arithmetic. AUTO picks the faster one measured on MI355X. */
+/* Split-kernel arithmetic.  MFMA (matrix cores): head_dim 128, G <= 16.
+ * VALU (vector ALU): head_dim 64 or 128, G <= 8.  AUTO, the faster one
+ * measured on MI355X: MFMA for head_dim 128, VALU for head_dim 64 (so G <= 8
+ * there).  pkv_decode returns PKV_ESHAPE for any other combination. */
 enum { PKV_KERNEL_AUTO = 0, PKV_KERNEL_VALU = 1, PKV_KERNEL_MFMA = 2 };
 
 typedef struct pkv_problem {

@@ -26,6 +26,15 @@ pkv_status check_plan(const pkv_problem* prob, const void* plan_host, const int3
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Shapes the chosen split kernel covers: matrix cores d = 128, G <= 16;
+// vector ALU d = 64 or 128, G <= 8; AUTO is matrix cores for d = 128.
+pkv_status check_kernel_shape(const pkv_problem* p) {
+  const int g = p->num_q_heads / p->num_kv_heads;
+  const bool mfma = p->kernel == PKV_KERNEL_MFMA || (p->kernel == PKV_KERNEL_AUTO && p->head_dim == 128);
+  if (mfma) return (p->head_dim == 128 && g <= kMaxGroup) ? PKV_OK : PKV_ESHAPE;
+  return g <= 8 ? PKV_OK : PKV_ESHAPE;
+}
+
 }  // namespace
 
 extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
@@ -39,6 +48,8 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
   st = check_plan(prob, plan_host, &w);
   if (st != PKV_OK) return st;
   if (!plan_dev || !q || !k_pool || !v_pool || !block_table || !seq_lens_dev) return PKV_EINVAL;
+  st = check_kernel_shape(prob);
+  if (st != PKV_OK) return st;
   const int path = w[kPath];
   if (path == PKV_NOSPLIT) {
     if (!out) return PKV_EINVAL;

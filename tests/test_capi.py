@@ -184,6 +184,16 @@ def test_decode_and_merge_validate_before_launch():
     with pytest.raises(PkvError) as e:  # missing states on a split path
         _lib.pkv_decode(prob, buf, fake, fake, fake, fake, fake, fake, None, None, None)
     assert e.value.status == PKV_EINVAL
+    # Kernel / shape combinations no split kernel covers, caught before launch.
+    for hq, hkv, d, kernel in ((32, 2, 64, _lib.PKV_KERNEL_AUTO),    # d=64 needs G <= 8
+                               (32, 2, 128, _lib.PKV_KERNEL_VALU),   # VALU: G <= 8
+                               (8, 2, 64, _lib.PKV_KERNEL_MFMA)):    # MFMA: d = 128 only
+        pr = _prob(2, hq=hq, hkv=hkv, d=d)
+        pr.kernel = kernel
+        pb = _plan_buf(pr, [40, 3], PKV_WORKQUEUE, 4)
+        with pytest.raises(PkvError) as e:
+            _lib.pkv_decode(pr, pb, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+        assert e.value.status == PKV_ESHAPE, (hq, hkv, d, kernel)
     bad = buf.copy()
     bad[0] = 0
     with pytest.raises(PkvError) as e:  # not a plan

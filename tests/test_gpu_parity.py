@@ -221,3 +221,21 @@ def test_policy_sweep_large_batches_sampled_rows(batch):
         check_out(step.out, ref_out, "bf16", rows=rows, label=f"policy_b{batch}/{path}:{s}")
         check_lse(step.lse, ref_lse, rows=rows, label=f"policy_b{batch}/{path}:{s}")
         assert torch.isfinite(step.out.float()).all()
+
+
+@pytest.mark.parametrize("hq,hkv,dtype", [(32, 2, "bf16"), (32, 2, "f16"), (8, 8, "f16")])
+def test_group_extremes_at_full_length(hq, hkv, dtype):
+    """G = 16 (the two-pages-in-flight matrix-core variant) and G = 1 (plain
+    multi-head decode) at long-context lengths, every path, on every row of a
+    4-row batch with mixed lengths."""
+    rng = np.random.default_rng(11)
+    lens = np.array([32768, int(rng.integers(16385, 32768)), int(rng.integers(1, 4096)), 17],
+                    dtype=np.int32)
+    spec = traces.custom_spec(4, hq, hkv, 128, splits=32, dtype=dtype)
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    say(f"[groups] hq={hq} hkv={hkv} {dtype} lens={lens.tolist()}")
+    ref_out, ref_lse = oracle_out(w)
+    for path, s in (("workqueue", 32), ("bucketed", 32), ("padded", 32), ("nosplit", 1)):
+        step, _ = _run(w, path, s, "auto")
+        check_out(step.out, ref_out, dtype, label=f"groups/{hq}/{hkv}/{path}")
+        check_lse(step.lse, ref_lse, label=f"groups/{hq}/{hkv}/{path}")
