@@ -125,6 +125,7 @@ typedef struct pkv_plan_info {
   int64_t kv_bytes;         /* bytes of real KV tokens: sum N_i*Hkv*d*2*e   */
   int64_t merge_state_bytes;/* 2 * slots * G * (d + 2) * 4: written + read  */
   int64_t plan_bytes;       /* bytes of the plan buffer actually used       */
+  int32_t max_task_pages;   /* pages of the longest task                    */
 } pkv_plan_info;
 
 /* Ordered policy rules, first match wins.  Row r is

@@ -75,6 +75,7 @@ class pkv_plan_info(ctypes.Structure):
         ("kv_bytes", ctypes.c_int64),
         ("merge_state_bytes", ctypes.c_int64),
         ("plan_bytes", ctypes.c_int64),
+        ("max_task_pages", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

@@ -34,6 +34,26 @@ constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxDevicePlanRows = 16384;  // batch limit of the device-side planner
 
+// Counters of a plan, computed from the lengths without writing it (the
+// host planner's counting pass; the cost model's features use it too).
+struct PlanCounts {
+  int64_t n_tasks;         // non-empty (row, kv head, split) tasks
+  int64_t n_slots;         // partial-state slots of the split launches
+  int64_t n_empty;         // slots holding only a neutral state
+  int32_t n_buckets;       // bucket launches (exact or padded buckets)
+  int32_t n_launches;      // kernel launches per step
+  int32_t pps;             // WORKQUEUE split granule (pages)
+  int32_t max_task_pages;  // pages of the longest task
+};
+
+// Rows in bucket order: ascending key (the exact length, or for padded
+// buckets the page count rounded up to a power of two), ties by row index.
+void order_rows(const int32_t* lens, int32_t b, bool padded, int32_t page_size, int32_t* order);
+// Counters of the plan pkv_plan would write; `order` (from order_rows) is
+// read for BUCKETED and PADDED only.  Lengths must already be validated.
+PlanCounts count_plan(const pkv_problem& p, const int32_t* lens, int32_t path, int32_t splits,
+                      const int32_t* order);
+
 // Which grid a split-kernel launch walks.
 enum SplitMode : int { kModeWorkqueue = 0, kModeBucket = 1, kModeNoSplit = 2, kModePersistent = 3 };
 

@@ -16,7 +16,6 @@
 #include <algorithm>
 #include <cstring>
 #include <numeric>
-#include <vector>
 
 #include "pkv_internal.h"
 
@@ -49,6 +48,87 @@ pkv_status check_problem(const pkv_problem* p) {
   if (p->kernel < PKV_KERNEL_AUTO || p->kernel > PKV_KERNEL_MFMA) return PKV_EINVAL;
   if (!(p->sm_scale == p->sm_scale)) return PKV_EINVAL;  // NaN scale
   return PKV_OK;
+}
+
+}  // namespace pkv
+
+namespace pkv {
+
+void order_rows(const int32_t* lens, int32_t b, bool padded, int32_t page_size, int32_t* order) {
+  for (int32_t i = 0; i < b; ++i) order[i] = i;
+  auto key = [&](int32_t r) -> int64_t {
+    return padded ? pow2_ceil(static_cast<int32_t>(ceil_div(lens[r], page_size))) : lens[r];
+  };
+  // Ties broken by row index: the same order as a stable sort, without the
+  // temporary buffer a stable sort may allocate.
+  std::sort(order, order + b, [&](int32_t x, int32_t y) {
+    const int64_t kx = key(x), ky = key(y);
+    return kx < ky || (kx == ky && x < y);
+  });
+}
+
+namespace {
+
+// Walks the buckets of a bucketed or padded plan in `order`:
+// f(first, end, length_word, bucket_pages, pps, bucket_nsplit, max_row_pages)
+// for the run order[first, end) of rows sharing one bucket key.
+template <class F>
+void for_each_bucket(const int32_t* lens, int32_t b, bool padded, int32_t page_size,
+                     int32_t splits, const int32_t* order, F&& f) {
+  for (int32_t k = 0; k < b;) {
+    const int32_t t0 = static_cast<int32_t>(ceil_div(lens[order[k]], page_size));
+    const int64_t key = padded ? pow2_ceil(t0) : lens[order[k]];
+    int32_t e = k, max_pages = 0;
+    while (e < b) {
+      const int32_t r = order[e];
+      const int32_t t = static_cast<int32_t>(ceil_div(lens[r], page_size));
+      if ((padded ? pow2_ceil(t) : lens[r]) != key) break;
+      max_pages = std::max(max_pages, t);
+      ++e;
+    }
+    const int32_t pages = padded ? static_cast<int32_t>(key) : t0;
+    const int32_t pps = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(pages, splits)));
+    const int32_t nsplit = static_cast<int32_t>(ceil_div(pages, pps));
+    f(k, e, padded ? -1 : lens[order[k]], pages, pps, nsplit, max_pages);
+    k = e;
+  }
+}
+
+}  // namespace
+
+PlanCounts count_plan(const pkv_problem& p, const int32_t* lens, int32_t path, int32_t splits,
+                      const int32_t* order) {
+  PlanCounts c{};
+  const int32_t b = p.batch, hkv = p.num_kv_heads, psz = p.page_size;
+  int32_t t_max = 0;
+  for (int32_t i = 0; i < b; ++i)
+    t_max = std::max(t_max, static_cast<int32_t>(ceil_div(lens[i], psz)));
+  if (path == PKV_WORKQUEUE) {
+    c.pps = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(t_max, splits)));
+    for (int32_t i = 0; i < b; ++i) c.n_tasks += int64_t(hkv) * ceil_div(ceil_div(lens[i], psz), c.pps);
+    c.n_slots = c.n_tasks;
+    c.n_launches = 1 + (c.n_tasks > 0 ? 1 : 0);
+    c.max_task_pages = std::min(c.pps, t_max);
+  } else if (path == PKV_NOSPLIT) {
+    for (int32_t i = 0; i < b; ++i) c.n_tasks += lens[i] > 0 ? hkv : 0;
+    c.n_launches = 1;
+    c.max_task_pages = t_max;
+  } else {
+    for_each_bucket(lens, b, path == PKV_PADDED, psz, splits, order,
+                    [&](int32_t first, int32_t end, int32_t, int32_t, int32_t pps, int32_t,
+                        int32_t max_pages) {
+                      for (int32_t j = first; j < end; ++j) {
+                        const int64_t ns = ceil_div(ceil_div(lens[order[j]], psz), pps);
+                        c.n_tasks += hkv * ns;
+                        c.n_empty += hkv * (splits - ns);
+                      }
+                      c.n_slots += int64_t(end - first) * hkv * splits;
+                      c.max_task_pages = std::max(c.max_task_pages, std::min(pps, max_pages));
+                      ++c.n_buckets;
+                    });
+    c.n_launches = 2 * c.n_buckets;
+  }
+  return c;
 }
 
 }  // namespace pkv
@@ -102,18 +182,33 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
   // Alignment words between row_task_off and the task list.
   for (int64_t i = PKV_PLAN_HEADER_WORDS + 4 * int64_t(b) + 1; i < off_tasks; ++i) w[i] = 0;
 
-  int32_t t_max = 0;
   for (int i = 0; i < b; ++i) {
     row_len[i] = seq_lens_host[i];
     row_pages[i] = static_cast<int32_t>(ceil_div(seq_lens_host[i], psz));
-    t_max = std::max(t_max, row_pages[i]);
   }
 
-  int64_t n_tasks = 0, n_slots = 0, n_empty = 0;
-  int32_t pps_global = 0;
-  int32_t n_buckets = 0;
-  std::vector<int32_t> order;
+  // Bucketed and padded plans order the rows by bucket key.  The order is
+  // built in the last B words the plan may use, then moved to its place in
+  // the plan (bucket_rows) once the task count fixes that place; the library
+  // allocates no memory of its own.
+  const bool bucketed = (path == PKV_BUCKETED || path == PKV_PADDED);
+  const int64_t upper = static_cast<int64_t>(words_upper_bound(prob, path, max_splits));
+  int32_t* order = nullptr;
+  if (bucketed) {
+    order = w + upper - b;
+    order_rows(seq_lens_host, b, path == PKV_PADDED, psz, order);
+  }
+  const PlanCounts c = count_plan(*prob, seq_lens_host, path, max_splits, order);
+  if (c.n_slots > INT32_MAX || c.n_tasks > INT32_MAX) return PKV_ERANGE;
+  const int64_t off_buckets = off_tasks + kTaskWords * c.n_tasks;
+  const int64_t off_brows = off_buckets + kBucketWords * int64_t(c.n_buckets);
+  const int64_t total = off_brows + (bucketed ? b : 0);
+  if (bucketed) {
+    std::memmove(w + off_brows, order, size_t(b) * sizeof(int32_t));
+    order = w + off_brows;  // tasks and buckets are written below this point
+  }
 
+  int64_t n_tasks = 0;
   // Word 3 is the task's token end min(pe * P, N_row), from which the
   // kernels get both the page end and the real tokens of the last page.
   auto push_task = [&](int row, int g, int s, int pb, int pe) {
@@ -126,74 +221,40 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
   };
 
   if (path == PKV_WORKQUEUE) {
-    pps_global = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(t_max, max_splits)));
     for (int i = 0; i < b; ++i) {
-      row_nsplit[i] = static_cast<int32_t>(ceil_div(row_pages[i], pps_global));
+      row_nsplit[i] = static_cast<int32_t>(ceil_div(row_pages[i], c.pps));
       row_task_off[i] = static_cast<int32_t>(n_tasks);
       for (int g = 0; g < hkv; ++g)
         for (int s = 0; s < row_nsplit[i]; ++s)
-          push_task(i, g, s, s * pps_global, std::min((s + 1) * pps_global, row_pages[i]));
+          push_task(i, g, s, s * c.pps, std::min((s + 1) * c.pps, row_pages[i]));
     }
     row_task_off[b] = static_cast<int32_t>(n_tasks);
-    n_slots = n_tasks;
-  } else if (path == PKV_BUCKETED || path == PKV_PADDED) {
-    const bool padded = (path == PKV_PADDED);
-    // Bucket key: the exact length, or the padded page count.
-    std::vector<int64_t> key(b);
-    for (int i = 0; i < b; ++i) key[i] = padded ? pow2_ceil(row_pages[i]) : seq_lens_host[i];
-    order.resize(b);
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return key[x] < key[y]; });
-    // Buckets and their rows are appended after the task list once its
-    // length is known; collect them first.
-    struct Bucket { int32_t len, pages, pps, nsplit, n_rows, first; };
-    std::vector<Bucket> bks;
-    for (int k = 0; k < b;) {
-      int e = k;
-      while (e < b && key[order[e]] == key[order[k]]) ++e;
-      Bucket bk;
-      bk.len = padded ? -1 : seq_lens_host[order[k]];
-      bk.pages = padded ? static_cast<int32_t>(key[order[k]]) : row_pages[order[k]];
-      bk.pps = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(bk.pages, max_splits)));
-      bk.nsplit = static_cast<int32_t>(ceil_div(bk.pages, bk.pps));
-      bk.n_rows = e - k;
-      bk.first = k;
-      bks.push_back(bk);
-      for (int j = k; j < e; ++j) {
-        const int row = order[j];
-        // Row-local bound: the row's own pages set its split count.
-        row_nsplit[row] = static_cast<int32_t>(ceil_div(row_pages[row], bk.pps));
-        for (int g = 0; g < hkv; ++g)
-          for (int s = 0; s < row_nsplit[row]; ++s)
-            push_task(row, g, s, s * bk.pps, std::min((s + 1) * bk.pps, row_pages[row]));
-        n_empty += int64_t(hkv) * (max_splits - row_nsplit[row]);
-      }
-      n_slots += int64_t(bk.n_rows) * hkv * max_splits;
-      k = e;
-    }
-    n_buckets = static_cast<int32_t>(bks.size());
-    // row_task_off: first task of each row in task order (rows appear in
-    // bucket order, so offsets are not monotone in the row index).
-    int64_t t = 0;
-    for (int j = 0; j < b; ++j) {
-      row_task_off[order[j]] = static_cast<int32_t>(t);
-      t += int64_t(hkv) * row_nsplit[order[j]];
-    }
-    row_task_off[b] = static_cast<int32_t>(t);
-    int32_t* bw = tasks + kTaskWords * n_tasks;
-    for (int k = 0; k < n_buckets; ++k) {
-      int32_t* e = bw + kBucketWords * k;
-      e[0] = bks[k].len;
-      e[1] = bks[k].pages;
-      e[2] = bks[k].pps;
-      e[3] = bks[k].nsplit;
-      e[4] = bks[k].n_rows;
-      e[5] = bks[k].first;
-      e[6] = 0;
-      e[7] = 0;
-    }
-    int32_t* brows = bw + kBucketWords * n_buckets;
-    for (int j = 0; j < b; ++j) brows[j] = order[j];
+  } else if (bucketed) {
+    int32_t* bw = w + off_buckets;
+    int32_t k = 0;
+    for_each_bucket(seq_lens_host, b, path == PKV_PADDED, psz, max_splits, order,
+                    [&](int32_t first, int32_t end, int32_t len_word, int32_t pages, int32_t pps,
+                        int32_t nsplit, int32_t) {
+                      for (int32_t j = first; j < end; ++j) {
+                        const int row = order[j];
+                        // Row-local bound: the row's own pages set its split count.
+                        row_nsplit[row] = static_cast<int32_t>(ceil_div(row_pages[row], pps));
+                        row_task_off[row] = static_cast<int32_t>(n_tasks);
+                        for (int g = 0; g < hkv; ++g)
+                          for (int s = 0; s < row_nsplit[row]; ++s)
+                            push_task(row, g, s, s * pps, std::min((s + 1) * pps, row_pages[row]));
+                      }
+                      int32_t* e = bw + kBucketWords * k++;
+                      e[0] = len_word;
+                      e[1] = pages;
+                      e[2] = pps;
+                      e[3] = nsplit;
+                      e[4] = end - first;
+                      e[5] = first;
+                      e[6] = 0;
+                      e[7] = 0;
+                    });
+    row_task_off[b] = static_cast<int32_t>(n_tasks);
   } else {  // PKV_NOSPLIT
     for (int i = 0; i < b; ++i) {
       row_nsplit[i] = row_pages[i] ? 1 : 0;
@@ -203,22 +264,18 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
     }
     row_task_off[b] = static_cast<int32_t>(n_tasks);
   }
-  if (n_slots > INT32_MAX) return PKV_ERANGE;
-
-  const int64_t off_buckets = off_tasks + kTaskWords * n_tasks;
-  const int64_t off_brows = off_buckets + kBucketWords * int64_t(n_buckets);
-  const int64_t total = off_brows + (n_buckets > 0 ? b : 0);
+  if (n_tasks != c.n_tasks) return PKV_EINVAL;  // counting and writing disagree: a bug
 
   w[kMagic] = PKV_PLAN_MAGIC;
   w[kPath] = path;
   w[kBatch] = b;
   w[kNumKvHeads] = hkv;
   w[kSplits] = max_splits;
-  w[kPagesPerSplit] = pps_global;
+  w[kPagesPerSplit] = path == PKV_WORKQUEUE ? c.pps : 0;
   w[kNumTasks] = static_cast<int32_t>(n_tasks);
-  w[kNumBuckets] = n_buckets;
-  w[kNumStateSlots] = static_cast<int32_t>(n_slots);
-  w[kNumEmptySlots] = static_cast<int32_t>(n_empty);
+  w[kNumBuckets] = c.n_buckets;
+  w[kNumStateSlots] = static_cast<int32_t>(c.n_slots);
+  w[kNumEmptySlots] = static_cast<int32_t>(c.n_empty);
   w[kOffTasks] = static_cast<int32_t>(off_tasks);
   w[kOffBuckets] = static_cast<int32_t>(off_buckets);
   w[kOffBucketRows] = static_cast<int32_t>(off_brows);
@@ -270,5 +327,11 @@ extern "C" pkv_status pkv_plan_get_info(const pkv_problem* prob, const void* pla
   info->kv_bytes = tokens * prob->num_kv_heads * prob->head_dim * 2 * 2;
   info->merge_state_bytes = 2 * int64_t(w[kNumStateSlots]) * g * (prob->head_dim + 2) * 4;
   info->plan_bytes = int64_t(w[kTotalWords]) * 4;
+  const int32_t* tasks = w + w[kOffTasks];
+  for (int32_t j = 0; j < w[kNumTasks]; ++j) {
+    const int32_t pages = (tasks[kTaskWords * j + 3] + prob->page_size - 1) / prob->page_size -
+                          tasks[kTaskWords * j + 2];
+    info->max_task_pages = std::max(info->max_task_pages, pages);
+  }
   return PKV_OK;
 }

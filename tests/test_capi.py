@@ -79,8 +79,15 @@ def test_host_planner_matches_oracle_bit_exactly(seed, path):
     assert info.merge_state_bytes == ref.merge_state_bytes
     assert info.n_buckets == len(ref.buckets)
     assert info.plan_bytes == got["total_words"] * 4
+    assert info.max_task_pages == max((pe - pb for *_, pb, pe in ref.tasks), default=0)
     again = _lib.pkv_plan_get_info(prob, _plan_buf(prob, lens, path, s))
     assert again.as_dict() == info.as_dict()
+    # The planner uses the buffer's tail as scratch: prior contents must not matter.
+    dirty = np.full(_lib.pkv_plan_bytes(prob, path, s) // 4, -12345, dtype=np.int32)
+    _lib.pkv_plan(prob, np.asarray(lens, dtype=np.int32), path, s, dirty)
+    clean = _plan_buf(prob, lens, path, s)
+    n = got["total_words"]
+    np.testing.assert_array_equal(dirty[:n], clean[:n])
 
 
 def _plan_buf(prob, lens, path, s):
