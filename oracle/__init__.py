@@ -20,6 +20,8 @@ what the PersistentKV summary pages define:
   ("2. Calibrated adaptive policy").
 * ``append_kv`` -- storing a step's new key/value through the block table
   (the input side of the decode step; not described on the pages).
+* ``cost`` -- plan features and the argmin choice of a learned per-path
+  linear cost model (future work on the pages, "Conclusion").
 """
 from .attention import (  # noqa: F401
     attention,
@@ -32,5 +34,6 @@ from .attention import (  # noqa: F401
     split_states_for_plan,
 )
 from .append import append_kv  # noqa: F401
+from . import cost  # noqa: F401
 from .planner import plan, pages_of  # noqa: F401
 from .policy import choose  # noqa: F401
