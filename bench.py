@@ -1,7 +1,7 @@
 """Decode-attention benchmark: µs per decode step and achieved HBM GB/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
-                    [--path bucketed|workqueue|nosplit|padded|policy] [--kernel auto|valu|mfma]
+                    [--path bucketed|workqueue|nosplit|padded|policy|model] [--kernel auto|valu|mfma]
 
 One step is the engine's device work for one decode step of one layer: the
 split kernel launch(es) and the merge launch(es) (or the single no-split
@@ -153,6 +153,7 @@ def run_all(args) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rules = engine.load_policy_table()
+    cost_model = engine.load_cost_model()
     for name in ALL_CONFIGS:
         spec = traces.get_spec(name)
         w = traces.generate(spec, traces.HELD_OUT_SEED)
@@ -161,10 +162,12 @@ def run_all(args) -> int:
         engine.validate_inputs(wd)
         views = timing.pool_copies(wd, args.copies_gib, max_copies=8)
         pol = engine.choose(rules, spec.batch, int(lens.max()))
+        mod = engine.choose_model(cost_model, engine.problem_from_workload(w), lens)[:2]
         cands = [("bucketed", spec.splits), ("workqueue", spec.splits), ("nosplit", 1),
                  ("padded", spec.splits)]
-        if pol not in cands:
-            cands.append(pol)
+        for c in (pol, mod):
+            if c not in cands:
+                cands.append(c)
         cpu = None if args.no_cpu_baseline else cpu_baseline(w, min(args.cpu_budget_s, 5.0))
         pr = timing.time_read_probe(w, views, "workqueue", spec.splits, args.steps, args.warmup)
         print(json.dumps({"workload": describe(spec, "read-only probe", spec.splits, lens),
@@ -194,7 +197,7 @@ def run_all(args) -> int:
             gbs = kv / (r["step_us"] * 1e-6) / 1e9
             print(json.dumps({
                 "workload": describe(spec, path, s, lens), "config": name, "path": path,
-                "splits": s, "policy_choice": (path, s) == pol,
+                "splits": s, "policy_choice": (path, s) == pol, "model_choice": (path, s) == mod,
                 "us_per_step": round(r["step_us"], 2), "GB/s": round(gbs, 1),
                 "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                 "split_us_per_launch": round(r["split_us"] / max(1, r["n_split_launches"]), 2),
@@ -232,6 +235,9 @@ def main(argv=None):
     if path == "policy":
         rules = engine.load_policy_table()
         path, splits = engine.choose(rules, spec.batch, int(lens.max()))
+    elif path == "model":  # the learned cost model's choice
+        path, splits, _ = engine.choose_model(engine.load_cost_model(),
+                                              engine.problem_from_workload(w), lens)
     wd = engine.to_device(w)
     engine.validate_inputs(wd)
 

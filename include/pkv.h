@@ -243,32 +243,42 @@ pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void*
  * Learned cost model (an alternative to the threshold table; the pages leave
  * a learned model as future work, "Conclusion").  For a candidate
  * (path, split cap) the features f[0..PKV_COST_FEATURES) of its plan are
- *   f0 = 1, f1 = log2 B, f2 = log2 max(1, N_max), f3 = log2 max(1, mean N_i),
- *   f4 = log2 S (0 for NOSPLIT), f5 = log2 max(1, n_tasks), f6 = launches per
- *   step, f7 = log2 max(1, grid items: n_tasks for WORKQUEUE, B * Hkv for
- *   NOSPLIT, n_state_slots for the bucket paths), f8 = log2(1 + merge state
- *   bytes), f9 = log2 max(1, real-KV bytes), f10 = log2 max(1, pages of the
- *   longest task),
- * with the counters pkv_plan would report, and the model predicts
- * log2(step microseconds) = sum_j weights[path][j] * f_j.  pkv_policy_model
+ *   f0 = 1
+ *   f1 = kernel launches per step
+ *   f2 = real-KV megabytes, sum N_i * Hkv * d * 2 * 2 / 1e6
+ *   f3 = merge-state megabytes, 2 * n_state_slots * G * (d + 2) * 4 / 1e6
+ *   f4 = per-CU critical pages: for each split launch, grid item j (the
+ *        launch's workgroups in grid order: tasks for WORKQUEUE, (row, kv
+ *        head) for NOSPLIT, (bucket row, kv head, split slot) for the bucket
+ *        paths, empty slots counting 0 pages) is charged to CU j mod num_cus;
+ *        f4 sums over the launches the largest page total of one CU
+ *   f5 = grid items of all split launches / 1000
+ *   f6 = non-empty tasks / 1000
+ * with the counters pkv_plan would report, and the model predicts the step
+ * time in microseconds as sum_j weights[path][j] * f_j.  pkv_policy_model
  * returns the candidate with the smallest prediction (the first one on a
- * tie) and, when predicted_us_out is not NULL, its predicted time.
+ * tie) and, when predicted_us_out is not NULL, that prediction.
+ * num_cus (1..1024): the device's compute units the model was fitted with.
  * scratch_host: B int32 of caller memory, used for bucket orders (may be
- * NULL when no candidate is BUCKETED or PADDED).  Host only, nothing is
- * enqueued.  Errors: PKV_EINVAL (null pointer, empty model, a candidate with
- * an unknown path or a split cap outside [1, 65535]), PKV_ESHAPE, PKV_EDTYPE,
- * PKV_ERANGE (a length outside [0, max_pages_per_row * P]).
+ * NULL when no candidate is BUCKETED or PADDED).  NOSPLIT candidates ignore
+ * their split cap.  Host only, nothing is enqueued; cost O(B + tasks) per
+ * candidate.  Errors: PKV_EINVAL (null pointer, empty model, num_cus out of
+ * range, a candidate with an unknown path or a split cap outside
+ * [1, 65535]), PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE (a length outside
+ * [0, max_pages_per_row * P]).
  */
-#define PKV_COST_FEATURES 11
+#define PKV_COST_FEATURES 7
 
 typedef struct pkv_cost_model {
   int32_t n_candidates;
   const int32_t* candidates; /* [n_candidates][2] = { path, split cap }       */
   const float* weights;      /* [4][PKV_COST_FEATURES], one row per path id   */
+  int32_t num_cus;           /* compute units used for feature f4             */
 } pkv_cost_model;
 
 pkv_status pkv_cost_features(const pkv_problem* prob, const int32_t* seq_lens_host, int32_t path,
-                             int32_t max_splits, int32_t* scratch_host, float* features_out);
+                             int32_t max_splits, int32_t num_cus, int32_t* scratch_host,
+                             float* features_out);
 pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_model* model,
                             const int32_t* seq_lens_host, int32_t* scratch_host,
                             int32_t* path_out, int32_t* splits_out, float* predicted_us_out);

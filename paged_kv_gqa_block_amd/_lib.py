@@ -39,7 +39,7 @@ KERNEL_IDS = {"auto": PKV_KERNEL_AUTO, "valu": PKV_KERNEL_VALU, "mfma": PKV_KERN
 EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pkv_merge",
             "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_append_kv",
             "pkv_policy", "pkv_cost_features", "pkv_policy_model", "pkv_status_str")
-PKV_COST_FEATURES = 11
+PKV_COST_FEATURES = 7
 
 
 class PkvError(RuntimeError):
@@ -89,7 +89,7 @@ class pkv_policy_table(ctypes.Structure):
 
 class pkv_cost_model(ctypes.Structure):
     _fields_ = [("n_candidates", ctypes.c_int32), ("candidates", ctypes.POINTER(ctypes.c_int32)),
-                ("weights", ctypes.POINTER(ctypes.c_float))]
+                ("weights", ctypes.POINTER(ctypes.c_float)), ("num_cus", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -122,7 +122,7 @@ def _load() -> ctypes.CDLL:
     lib.pkv_policy.argtypes = [ctypes.POINTER(pkv_policy_table), i32, i32,
                                ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.pkv_policy.restype = i32
-    lib.pkv_cost_features.argtypes = [prob_p, vp, i32, i32, vp, vp]
+    lib.pkv_cost_features.argtypes = [prob_p, vp, i32, i32, i32, vp, vp]
     lib.pkv_cost_features.restype = i32
     lib.pkv_policy_model.argtypes = [prob_p, ctypes.POINTER(pkv_cost_model), vp, vp,
                                      ctypes.POINTER(i32), ctypes.POINTER(i32), f32p]
@@ -272,17 +272,18 @@ def pkv_policy(rules, batch: int, max_len: int):
     return path.value, splits.value
 
 
-def pkv_cost_features(prob: pkv_problem, seq_lens_host, path: int, max_splits: int) -> np.ndarray:
+def pkv_cost_features(prob: pkv_problem, seq_lens_host, path: int, max_splits: int,
+                      num_cus: int) -> np.ndarray:
     lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
     scratch = np.empty(max(1, prob.batch), dtype=np.int32)
     out = np.empty(PKV_COST_FEATURES, dtype=np.float32)
     _check("pkv_cost_features", LIB.pkv_cost_features(
-        ctypes.byref(prob), lens.ctypes.data, path, max_splits, scratch.ctypes.data,
+        ctypes.byref(prob), lens.ctypes.data, path, max_splits, num_cus, scratch.ctypes.data,
         out.ctypes.data))
     return out
 
 
-def pkv_policy_model(prob: pkv_problem, candidates, weights, seq_lens_host):
+def pkv_policy_model(prob: pkv_problem, candidates, weights, num_cus: int, seq_lens_host):
     """candidates: [(path_id, splits)]; weights: [4][PKV_COST_FEATURES].
     Returns (path_id, splits, predicted_us)."""
     cand = np.ascontiguousarray(np.asarray(candidates, dtype=np.int32).reshape(-1))
@@ -290,7 +291,7 @@ def pkv_policy_model(prob: pkv_problem, candidates, weights, seq_lens_host):
     if w.size != 4 * PKV_COST_FEATURES:
         raise ValueError("weights must be [4][PKV_COST_FEATURES]")
     model = pkv_cost_model(len(cand) // 2, cand.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                           w.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+                           w.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), num_cus)
     lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
     scratch = np.empty(max(1, prob.batch), dtype=np.int32)
     path, splits, pred = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_float()

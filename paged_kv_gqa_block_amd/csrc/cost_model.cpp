@@ -1,9 +1,9 @@
 // Learned cost model for the path choice: plan features of a candidate
-// (path, split cap) and a per-path linear model of log2 of the step time,
-// fitted by least squares to measured step times.  The PersistentKV summary
-// pages leave such a model as future work ("Conclusion"; "2. Calibrated
-// adaptive policy" uses hand-calibrated thresholds instead).  Host code only;
-// it allocates nothing (bucket orders use the caller's scratch).
+// (path, split cap) in natural units and a per-path linear model of the step
+// time, fitted to measured step times.  The PersistentKV summary pages leave
+// such a model as future work ("Conclusion"; "2. Calibrated adaptive policy"
+// uses hand-calibrated thresholds instead).  Host code only; it allocates
+// nothing (bucket orders use the caller's scratch, per-CU sums the stack).
 #include <algorithm>
 #include <cmath>
 
@@ -13,56 +13,97 @@ using namespace pkv;
 
 namespace {
 
-double log2_at_least_1(double x) { return std::log2(std::max(1.0, x)); }
+constexpr int kMaxCus = 1024;
+
+// Per-CU load of one launch: grid item j goes to CU j mod num_cus (the
+// round-robin spread of a launch's workgroups); returns the largest sum of
+// pages over the CUs.
+struct CuLoad {
+  int64_t acc[kMaxCus];
+  int32_t cus;
+  int64_t j;
+  void start(int32_t n) {
+    cus = n;
+    j = 0;
+    std::fill(acc, acc + n, 0);
+  }
+  void add(int64_t pages) { acc[j++ % cus] += pages; }
+  int64_t max() const { return *std::max_element(acc, acc + cus); }
+};
 
 pkv_status features(const pkv_problem* prob, const int32_t* lens, int32_t path, int32_t splits,
-                    int32_t* scratch, float* f) {
-  const int32_t b = prob->batch, hkv = prob->num_kv_heads;
-  const int64_t cap = int64_t(prob->max_pages_per_row) * prob->page_size;
-  int64_t sum = 0;
-  int32_t n_max = 0;
-  for (int32_t i = 0; i < b; ++i) {
+                    int32_t num_cus, int32_t* scratch, float* f) {
+  const int32_t b = prob->batch, hkv = prob->num_kv_heads, psz = prob->page_size;
+  const int64_t cap = int64_t(prob->max_pages_per_row) * psz;
+  for (int32_t i = 0; i < b; ++i)
     if (lens[i] < 0 || lens[i] > cap) return PKV_ERANGE;
-    sum += lens[i];
-    n_max = std::max(n_max, lens[i]);
-  }
   const bool bucketed = (path == PKV_BUCKETED || path == PKV_PADDED);
   if (bucketed) {
     if (!scratch) return PKV_EINVAL;
-    order_rows(lens, b, path == PKV_PADDED, prob->page_size, scratch);
+    order_rows(lens, b, path == PKV_PADDED, psz, scratch);
   }
   const PlanCounts c = count_plan(*prob, lens, path, splits, bucketed ? scratch : nullptr);
+
+  // Grid items in launch order with their pages (0 for an empty slot).
+  CuLoad load;  // 8 KiB on the stack
+  int64_t crit = 0, items = 0;
+  load.start(num_cus);
+  if (path == PKV_WORKQUEUE) {
+    for (int32_t i = 0; i < b; ++i) {
+      const int64_t t = ceil_div(lens[i], psz);
+      const int64_t ns = ceil_div(t, c.pps);
+      for (int32_t g = 0; g < hkv; ++g)
+        for (int64_t s = 0; s < ns; ++s) load.add(std::min<int64_t>(c.pps, t - s * c.pps));
+    }
+    items = load.j;
+    crit = load.max();
+  } else if (path == PKV_NOSPLIT) {
+    for (int32_t i = 0; i < b; ++i)
+      for (int32_t g = 0; g < hkv; ++g) load.add(ceil_div(lens[i], psz));
+    items = load.j;
+    crit = load.max();
+  } else {
+    for_each_bucket(lens, b, path == PKV_PADDED, psz, splits, scratch,
+                    [&](int32_t first, int32_t end, int32_t, int32_t, int32_t pps, int32_t,
+                        int32_t) {
+                      load.start(num_cus);
+                      for (int32_t r = first; r < end; ++r) {
+                        const int64_t t = ceil_div(lens[scratch[r]], psz);
+                        for (int32_t g = 0; g < hkv; ++g)
+                          for (int32_t s = 0; s < splits; ++s)
+                            load.add(std::max<int64_t>(0, std::min<int64_t>(pps, t - int64_t(s) * pps)));
+                      }
+                      items += load.j;
+                      crit += load.max();
+                    });
+  }
+  int64_t tokens = 0;
+  for (int32_t i = 0; i < b; ++i) tokens += lens[i];
   const int64_t g = prob->num_q_heads / hkv;
-  const double items = path == PKV_WORKQUEUE ? double(c.n_tasks)
-                       : path == PKV_NOSPLIT ? double(b) * hkv
-                                             : double(c.n_slots);
-  const double state_bytes = 2.0 * double(c.n_slots) * g * (prob->head_dim + 2) * 4;
-  const double kv_bytes = double(sum) * hkv * prob->head_dim * 2 * 2;
   f[0] = 1.f;
-  f[1] = float(log2_at_least_1(b));
-  f[2] = float(log2_at_least_1(n_max));
-  f[3] = float(log2_at_least_1(double(sum) / b));
-  f[4] = float(log2_at_least_1(path == PKV_NOSPLIT ? 1 : splits));
-  f[5] = float(log2_at_least_1(double(c.n_tasks)));
-  f[6] = float(c.n_launches);
-  f[7] = float(log2_at_least_1(items));
-  f[8] = float(std::log2(1.0 + state_bytes));
-  f[9] = float(log2_at_least_1(kv_bytes));
-  f[10] = float(log2_at_least_1(c.max_task_pages));
+  f[1] = float(c.n_launches);
+  f[2] = float(double(tokens) * hkv * prob->head_dim * 2 * 2 / 1e6);
+  f[3] = float(2.0 * double(c.n_slots) * g * (prob->head_dim + 2) * 4 / 1e6);
+  f[4] = float(crit);
+  f[5] = float(double(items) / 1e3);
+  f[6] = float(double(c.n_tasks) / 1e3);
   return PKV_OK;
 }
+
+bool valid_cus(int32_t n) { return n >= 1 && n <= kMaxCus; }
 
 }  // namespace
 
 extern "C" pkv_status pkv_cost_features(const pkv_problem* prob, const int32_t* seq_lens_host,
-                                        int32_t path, int32_t max_splits, int32_t* scratch_host,
-                                        float* features_out) {
+                                        int32_t path, int32_t max_splits, int32_t num_cus,
+                                        int32_t* scratch_host, float* features_out) {
   pkv_status st = check_problem(prob);
   if (st != PKV_OK) return st;
   if (!seq_lens_host || !features_out) return PKV_EINVAL;
   if (path < PKV_BUCKETED || path > PKV_PADDED) return PKV_EINVAL;
-  if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
-  return features(prob, seq_lens_host, path, max_splits, scratch_host, features_out);
+  if (max_splits < 1 || max_splits > 65535 || !valid_cus(num_cus)) return PKV_EINVAL;
+  return features(prob, seq_lens_host, path, path == PKV_NOSPLIT ? 1 : max_splits, num_cus,
+                  scratch_host, features_out);
 }
 
 extern "C" pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_model* model,
@@ -72,28 +113,31 @@ extern "C" pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_m
   pkv_status st = check_problem(prob);
   if (st != PKV_OK) return st;
   if (!model || !seq_lens_host || !path_out || !splits_out) return PKV_EINVAL;
-  if (model->n_candidates < 1 || !model->candidates || !model->weights) return PKV_EINVAL;
+  if (model->n_candidates < 1 || !model->candidates || !model->weights ||
+      !valid_cus(model->num_cus))
+    return PKV_EINVAL;
   for (int32_t k = 0; k < model->n_candidates; ++k) {
     const int32_t path = model->candidates[2 * k], s = model->candidates[2 * k + 1];
     if (path < PKV_BUCKETED || path > PKV_PADDED || s < 1 || s > 65535) return PKV_EINVAL;
   }
   double best = INFINITY;
-  int32_t best_k = -1;
+  int32_t best_k = 0;
   float f[PKV_COST_FEATURES];
   for (int32_t k = 0; k < model->n_candidates; ++k) {
     const int32_t path = model->candidates[2 * k], s = model->candidates[2 * k + 1];
-    st = features(prob, seq_lens_host, path, s, scratch_host, f);
+    st = features(prob, seq_lens_host, path, path == PKV_NOSPLIT ? 1 : s, model->num_cus,
+                  scratch_host, f);
     if (st != PKV_OK) return st;
     const float* w = model->weights + PKV_COST_FEATURES * path;
     double y = 0.0;
     for (int j = 0; j < PKV_COST_FEATURES; ++j) y += double(w[j]) * f[j];
-    if (y < best) {  // first candidate wins ties
+    if (y < best) {  // the first candidate wins a tie
       best = y;
       best_k = k;
     }
   }
   *path_out = model->candidates[2 * best_k];
   *splits_out = model->candidates[2 * best_k + 1];
-  if (predicted_us_out) *predicted_us_out = float(std::exp2(best));
+  if (predicted_us_out) *predicted_us_out = float(best);
   return PKV_OK;
 }

@@ -2,6 +2,7 @@
 // kernel launchers of libpkv.  Not part of the public ABI (see include/pkv.h).
 #pragma once
 
+#include <algorithm>
 #include <cstdint>
 
 #include "pkv.h"
@@ -45,6 +46,41 @@ struct PlanCounts {
   int32_t pps;             // WORKQUEUE split granule (pages)
   int32_t max_task_pages;  // pages of the longest task
 };
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Smallest power of two >= t (0 for t = 0).
+inline int32_t pow2_ceil(int32_t t) {
+  int32_t p = 1;
+  if (t == 0) return 0;
+  while (p < t) p <<= 1;
+  return p;
+}
+
+// Walks the buckets of a bucketed or padded plan in `order`:
+// f(first, end, length_word, bucket_pages, pps, bucket_nsplit, max_row_pages)
+// for the run order[first, end) of rows sharing one bucket key.
+template <class F>
+void for_each_bucket(const int32_t* lens, int32_t b, bool padded, int32_t page_size,
+                     int32_t splits, const int32_t* order, F&& f) {
+  for (int32_t k = 0; k < b;) {
+    const int32_t t0 = static_cast<int32_t>(ceil_div(lens[order[k]], page_size));
+    const int64_t key = padded ? pow2_ceil(t0) : lens[order[k]];
+    int32_t e = k, max_pages = 0;
+    while (e < b) {
+      const int32_t r = order[e];
+      const int32_t t = static_cast<int32_t>(ceil_div(lens[r], page_size));
+      if ((padded ? pow2_ceil(t) : lens[r]) != key) break;
+      max_pages = std::max(max_pages, t);
+      ++e;
+    }
+    const int32_t pages = padded ? static_cast<int32_t>(key) : t0;
+    const int32_t pps = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(pages, splits)));
+    const int32_t nsplit = static_cast<int32_t>(ceil_div(pages, pps));
+    f(k, e, padded ? -1 : lens[order[k]], pages, pps, nsplit, max_pages);
+    k = e;
+  }
+}
 
 // Rows in bucket order: ascending key (the exact length, or for padded
 // buckets the page count rounded up to a power of two), ties by row index.

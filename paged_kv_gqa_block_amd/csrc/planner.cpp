@@ -20,19 +20,6 @@
 #include "pkv_internal.h"
 
 namespace pkv {
-namespace {
-
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Smallest power of two >= t (0 for t = 0).
-inline int32_t pow2_ceil(int32_t t) {
-  int32_t p = 1;
-  if (t == 0) return 0;
-  while (p < t) p <<= 1;
-  return p;
-}
-
-}  // namespace
 
 pkv_status check_problem(const pkv_problem* p) {
   if (!p) return PKV_EINVAL;
@@ -66,35 +53,6 @@ void order_rows(const int32_t* lens, int32_t b, bool padded, int32_t page_size, 
     return kx < ky || (kx == ky && x < y);
   });
 }
-
-namespace {
-
-// Walks the buckets of a bucketed or padded plan in `order`:
-// f(first, end, length_word, bucket_pages, pps, bucket_nsplit, max_row_pages)
-// for the run order[first, end) of rows sharing one bucket key.
-template <class F>
-void for_each_bucket(const int32_t* lens, int32_t b, bool padded, int32_t page_size,
-                     int32_t splits, const int32_t* order, F&& f) {
-  for (int32_t k = 0; k < b;) {
-    const int32_t t0 = static_cast<int32_t>(ceil_div(lens[order[k]], page_size));
-    const int64_t key = padded ? pow2_ceil(t0) : lens[order[k]];
-    int32_t e = k, max_pages = 0;
-    while (e < b) {
-      const int32_t r = order[e];
-      const int32_t t = static_cast<int32_t>(ceil_div(lens[r], page_size));
-      if ((padded ? pow2_ceil(t) : lens[r]) != key) break;
-      max_pages = std::max(max_pages, t);
-      ++e;
-    }
-    const int32_t pages = padded ? static_cast<int32_t>(key) : t0;
-    const int32_t pps = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(pages, splits)));
-    const int32_t nsplit = static_cast<int32_t>(ceil_div(pages, pps));
-    f(k, e, padded ? -1 : lens[order[k]], pages, pps, nsplit, max_pages);
-    k = e;
-  }
-}
-
-}  // namespace
 
 PlanCounts count_plan(const pkv_problem& p, const int32_t* lens, int32_t path, int32_t splits,
                       const int32_t* order) {

@@ -20,6 +20,7 @@ from ._lib import (PATH_IDS, PATH_NAMES, PKV_NOSPLIT, PKV_WORKQUEUE, make_proble
 
 TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
 POLICY_TABLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "policy_table.json")
+COST_MODEL_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "cost_model.json")
 
 
 def problem_from_workload(w: dict, kernel: str = "auto") -> _lib.pkv_problem:
@@ -136,6 +137,25 @@ def choose(rules, batch: int, max_len: int):
     """Path name and split cap from the calibrated table (C-ABI pkv_policy)."""
     path, splits = pkv_policy(rules, batch, max_len)
     return PATH_NAMES[path], splits
+
+
+def load_cost_model(path: str = COST_MODEL_PATH):
+    """(candidates [(path_id, splits)], weights [4][PKV_COST_FEATURES], num_cus)."""
+    with open(path) as f:
+        doc = json.load(f)
+    cands = [(PATH_IDS[c["path"]], c["splits"]) for c in doc["candidates"]]
+    weights = np.zeros((4, _lib.PKV_COST_FEATURES), dtype=np.float32)
+    for name, row in doc["weights"].items():
+        weights[PATH_IDS[name]] = np.asarray(row, dtype=np.float32)
+    return cands, weights, int(doc["num_cus"])
+
+
+def choose_model(model, prob: _lib.pkv_problem, seq_lens_host):
+    """Path name, split cap and predicted µs from the learned cost model
+    (C-ABI pkv_policy_model)."""
+    cands, weights, num_cus = model
+    path, splits, pred = _lib.pkv_policy_model(prob, cands, weights, num_cus, seq_lens_host)
+    return PATH_NAMES[path], splits, pred
 
 
 def validate_inputs(w: dict) -> None:

@@ -1,0 +1,56 @@
+"""The shipped learned cost model (CPU): its file is well formed, it was fitted
+on the calibration seed's timings, the C choice equals the oracle's on the
+sweep and trace workloads, and (once measured) the recorded held-out check."""
+import json
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_gqa_block_amd import _lib, engine, traces
+
+
+def _doc():
+    with open(engine.COST_MODEL_PATH) as f:
+        return json.load(f)
+
+
+def test_model_file_is_well_formed():
+    doc = _doc()
+    assert doc["trained_on"]["seed"] == traces.CALIBRATION_SEED
+    assert doc["num_cus"] == 256
+    cands, weights, cus = engine.load_cost_model()
+    assert len(cands) >= 4 and all(p in _lib.PATH_NAMES and s >= 1 for p, s in cands)
+    assert weights.shape == (4, _lib.PKV_COST_FEATURES) and np.isfinite(weights).all()
+    assert abs(weights).max() < 1e3  # the ridge term keeps weights moderate
+    fit = doc["fit"]
+    assert fit["rms_relative_error"] < 0.2
+    assert fit["5fold"]["over_best"] < 0.05
+
+
+@pytest.mark.parametrize("name", ["tiny", "long", "bimodal", "zipf", "uniform", "policy_b1",
+                                  "policy_b8", "policy_b64", "policy_short_b16"])
+def test_c_choice_equals_oracle_on_workloads(name):
+    spec = traces.get_spec(name)
+    lens = traces.draw_lengths(spec, np.random.default_rng(traces.HELD_OUT_SEED))
+    cands, weights, cus = engine.load_cost_model()
+    prob = _lib.make_problem(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                             spec.page_size, 1 << 20, 32768 // spec.page_size, spec.dtype)
+    path, s, pred = engine.choose_model((cands, weights, cus), prob, lens)
+    named = [(_lib.PATH_NAMES[p], ss) for p, ss in cands]
+    ref = oracle.cost.choose(weights.astype(np.float64), named, lens, spec.num_kv_heads,
+                             spec.num_q_heads, spec.head_dim, spec.page_size, cus)
+    assert (path, s) == ref[:2]
+    assert pred == pytest.approx(ref[2], rel=1e-5)
+    assert pred > 0
+
+
+def test_recorded_heldout_check():
+    doc = _doc()
+    if "heldout" not in doc:
+        pytest.skip("held-out measurement not recorded yet")
+    h = doc["heldout"]
+    assert h["seed"] == traces.HELD_OUT_SEED
+    for family in h["cells"].values():
+        for rec in family.values():
+            assert rec["model"] in rec["times"] and rec["table"] in rec["times"]
