@@ -206,7 +206,7 @@ def test_two_runs_are_bit_identical(kernel):
 @pytest.mark.parametrize("batch", (32, 64))
 def test_policy_sweep_large_batches_sampled_rows(batch):
     """Full-size B=32/64 bf16 sweep workloads in the launch configuration the
-    calibrated policy picks (and the three single paths); the oracle checks a
+    calibrated policy picks (and the four single paths); the oracle checks a
     sample of rows (first, a middle one, the longest, last)."""
     w = traces.generate(traces.get_spec(f"policy_b{batch}"), SEED)
     lens = w["seq_lens"].numpy()
