@@ -239,3 +239,28 @@ def test_group_extremes_at_full_length(hq, hkv, dtype):
         step, _ = _run(w, path, s, "auto")
         check_out(step.out, ref_out, dtype, label=f"groups/{hq}/{hkv}/{path}")
         check_lse(step.lse, ref_lse, label=f"groups/{hq}/{hkv}/{path}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_small_problems_every_path(seed):
+    """Random shapes, dtypes, split caps and lengths (with the page-boundary
+    values mixed in), every path and the kernel AUTO picks, element by element
+    against the oracle."""
+    rng = np.random.default_rng(4000 + seed)
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 8] + ([16] if d == 128 else [])))
+    b = int(rng.integers(1, 7))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    lens = rng.integers(0, 1200, size=b)
+    edge = rng.choice([0, 1, 15, 16, 17, 31, 32, 33], size=b)
+    lens = np.where(rng.random(b) < 0.4, edge, lens).astype(np.int32)
+    s = int(rng.choice([1, 2, 3, 5, 8, 32, 100]))
+    spec = traces.custom_spec(b, hkv * g, hkv, d, splits=s, dtype=dtype)
+    w = traces.generate(spec, SEED + seed, seq_lens=lens)
+    say(f"[random {seed}] B={b} Hq={hkv * g} Hkv={hkv} d={d} {dtype} S={s} lens={lens.tolist()}")
+    ref_out, ref_lse = oracle_out(w)
+    for path in PATHS:
+        step, _ = _run(w, path, 1 if path == "nosplit" else s, "auto")
+        check_out(step.out, ref_out, dtype, label=f"random{seed}/{path}")
+        check_lse(step.lse, ref_lse, label=f"random{seed}/{path}")
