@@ -200,6 +200,7 @@ def run_all(args) -> int:
                 "splits": s, "policy_choice": (path, s) == pol, "model_choice": (path, s) == mod,
                 "us_per_step": round(r["step_us"], 2), "GB/s": round(gbs, 1),
                 "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                "single_step_us": r["single_step_us"],
                 "split_us_per_launch": round(r["split_us"] / max(1, r["n_split_launches"]), 2),
                 "launches_per_step": r["info"]["n_launches"], "kv_bytes": kv,
                 "merge_state_bytes": r["info"]["merge_state_bytes"],
@@ -272,6 +273,7 @@ def main(argv=None):
                    "launches_per_step": info["n_launches"], "n_tasks": info["n_tasks"],
                    "kv_bytes": kv, "merge_state_bytes": info["merge_state_bytes"],
                    "pool_copies_rotated": len(views),
+                   "single_step_us": r["single_step_us"],
                    "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),

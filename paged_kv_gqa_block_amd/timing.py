@@ -72,6 +72,21 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
     split_us = statistics.median(split_runs)
     wall = statistics.median(walls)
 
+    # Distribution of single steps: an event pair around each step of one
+    # more loop (the events add a little time to each step, so the
+    # throughput figures above come from the back-to-back loops).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step.run(views[(warmup + i) % n], stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    single = sorted(1e3 * a.elapsed_time(b) for a, b in evs)
+
+    def pct(q):
+        return single[min(len(single) - 1, int(round(q * (len(single) - 1))))]
+
     # Synchronised wall time per step including host planning and the plan
     # upload (the pages' end-to-end latency metric).
     sync_us = []
@@ -92,6 +107,8 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         "step_us": step_us,
         "split_us": split_us,
         "step_us_runs": [round(x, 2) for x in step_runs],
+        "single_step_us": {"p10": round(pct(0.1), 2), "p50": round(pct(0.5), 2),
+                           "p90": round(pct(0.9), 2), "n": len(single)},
         "wall_ms_per_step": 1e3 * wall / steps,
         "sync_wall_us_median": statistics.median(sync_us) if sync_us else None,
         "out": step.out,
