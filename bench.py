@@ -35,7 +35,10 @@ HBM_PEAK_GBS = 8000.0
 # FETCH_SIZE + WRITE_SIZE runs, scaled against a copy kernel); reported only
 # while the kernel sources still hash to the value recorded with it.
 TRAFFIC_PROFILES = {"long": "profiles/split_mfma_long_b1_n32768_traffic.txt",
-                    "bimodal": "profiles/split_mfma_bimodal_b8_traffic.txt"}
+                    "bimodal": "profiles/split_mfma_bimodal_b8_traffic.txt",
+                    "zipf": "profiles/split_mfma_zipf_b8_traffic.txt",
+                    "uniform": "profiles/split_mfma_uniform_b8_traffic.txt",
+                    "policy_b64": "profiles/split_mfma_policy_b64_traffic.txt"}
 KERNEL_SOURCES = ("split_mfma.hip", "split_common.h", "device_common.h", "pkv_internal.h")
 DEFAULT_PATH = {"tiny": "workqueue", "long": "bucketed", "bimodal": "workqueue",
                 "zipf": "workqueue", "uniform": "workqueue"}
@@ -87,7 +90,7 @@ def recorded_traffic(config: str, kernel_used: str, path: str, splits: int, seed
     rel = TRAFFIC_PROFILES.get(config)
     if rel is None or kernel_used != "mfma":
         return None
-    if (path != DEFAULT_PATH.get(config) or splits != traces.get_spec(config).splits
+    if (path != DEFAULT_PATH.get(config, "workqueue") or splits != traces.get_spec(config).splits
             or seed != traces.HELD_OUT_SEED):
         return None
     try:
