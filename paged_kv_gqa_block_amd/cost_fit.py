@@ -1,5 +1,7 @@
 """Fit and check the learned cost model (an alternative to the threshold table).
 
+    python -m paged_kv_gqa_block_amd.cost_fit measure --hq 32 --hkv 8 --dtype f16
+                                                      # GPU: calibration timings, another shape
     python -m paged_kv_gqa_block_amd.cost_fit fit     # CPU: from stored calibration timings
     python -m paged_kv_gqa_block_amd.cost_fit check   # GPU: held-out measurement
 
@@ -15,42 +17,57 @@ per path on the relative error (each row scaled by 1 / measured time),
 with a small ridge term.  It also
 reports how the model's choices compare with the measured best, in sample,
 under 5-fold cross-validation over cells and leaving one batch size out.
-`check` measures, on held-out seed 20260623, the model's choice beside the
-table's choice and the four single paths, with interleaved repeats.
+`measure` times the same candidates on the same (B, N_max) grid and seed for
+another head shape / dtype and stores them beside the table
+(cost_calib_*.json); `fit` uses every such file too.  `check` measures, on
+held-out seed 20260623, the model's choice beside the table's choice and the
+four single paths, with interleaved repeats: on the two sweep families and on
+the trace workloads (another head shape and dtype).
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import json
+import os
 import sys
 import time
 
 import numpy as np
 
 from . import _lib, engine, traces
-from .calibrate import CANDIDATES, FAMILIES, NOISE, SINGLE_PATHS, cell_spec, log
+from .calibrate import CANDIDATES, FAMILIES, NOISE, SINGLE_PATHS, cell_spec, grid_of, log, measure
 
 PATHS = ("bucketed", "workqueue", "nosplit", "padded")
 RIDGE = 1e-3
 NUM_CUS = 256  # MI355X compute units: feature f4 deals grid items over them
 
 
-def sweep_problem(batch: int) -> _lib.pkv_problem:
+EXTRA_GLOB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "cost_calib_*.json")
+TRACE_WORKLOADS = ("long", "bimodal", "zipf", "uniform")
+
+
+def sweep_problem(batch: int, shape: dict | None = None) -> _lib.pkv_problem:
     base = traces.get_spec(f"policy_b{batch}")
-    return _lib.make_problem(batch, base.num_q_heads, base.num_kv_heads, base.head_dim,
-                             base.page_size, 1 << 20, 32768 // base.page_size, base.dtype)
+    shape = shape or {}
+    return _lib.make_problem(batch, shape.get("num_q_heads", base.num_q_heads),
+                             shape.get("num_kv_heads", base.num_kv_heads), base.head_dim,
+                             base.page_size, 1 << 20, 32768 // base.page_size,
+                             shape.get("dtype", base.dtype))
 
 
-def samples_from_table(table: dict):
+def samples_from_table(table: dict, shape: dict | None = None):
     """(cell, candidate, path, features, us) of every calibration timing."""
     out = []
+    tag = "" if not shape else f"{shape['num_q_heads']}/{shape['num_kv_heads']}/{shape['dtype']}:"
     for key, cell in table["calibration"].items():
         b, cap = cell["batch"], cell["cap"]
         lens = traces.draw_lengths(cell_spec(b, cap),
                                    np.random.default_rng(table["calibration_seed"]))
         if int(lens.max()) != cell["n_max"]:
             raise RuntimeError(f"cell {key}: regenerated lengths differ from the measured ones")
-        prob = sweep_problem(b)
+        prob = sweep_problem(b, shape)
+        key = tag + key
         for cand, t in cell["times"].items():
             path, s = cand.split(":")
             f = _lib.pkv_cost_features(prob, lens, _lib.PATH_IDS[path], int(s),
@@ -98,8 +115,13 @@ def cross_validate(samples) -> dict:
     res = {}
     for name, groups in (("5fold", folds),
                          ("leave_one_batch_out",
-                          [{c for c in cells if c.split(":")[0] == str(b)}
-                           for b in traces.POLICY_BATCHES])):
+                          [{c for c in cells if c.split(":")[-2] == str(b)}
+                           for b in traces.POLICY_BATCHES]),
+                         ("leave_one_shape_out",
+                          [{c for c in cells if c.count(":") == 1},
+                           {c for c in cells if c.count(":") > 1}])):
+        if any(not g for g in groups) or len(groups) < 2:
+            continue
         tot = {"model_total_us": 0.0, "best_total_us": 0.0, "cells_over_3pct": 0}
         for te in groups:
             q = choice_quality(fit([s for s in samples if s[0] not in te]),
@@ -113,17 +135,53 @@ def cross_validate(samples) -> dict:
     return res
 
 
-def cmd_fit(args) -> int:
-    with open(args.table) as f:
+def all_samples(table_path: str):
+    with open(table_path) as f:
         table = json.load(f)
-    samples = samples_from_table(table)
+    samples, sources = samples_from_table(table), ["policy_table.json"]
+    for path in sorted(glob.glob(EXTRA_GLOB)):
+        with open(path) as f:
+            extra = json.load(f)
+        samples += samples_from_table(extra, extra["shape"])
+        sources.append(os.path.basename(path))
+    return table, samples, sources
+
+
+def cmd_measure(args) -> int:
+    import torch
+
+    assert torch.cuda.is_available(), "measuring needs a GPU"
+    shape = {"num_q_heads": args.hq, "num_kv_heads": args.hkv, "dtype": args.dtype}
+    calib = {}
+    t0 = time.time()
+    for b in traces.POLICY_BATCHES:
+        for n in grid_of(b):
+            n_max, times = measure(cell_spec(b, n, args.hq, args.hkv, args.dtype),
+                                   traces.CALIBRATION_SEED, CANDIDATES, args.steps, args.warmup)
+            calib[f"{b}:{n}"] = {"batch": b, "cap": n, "n_max": n_max, "times": times}
+    doc = {"about": "Calibration timings of every candidate path on the (B, N_max) grid for "
+                    "one head shape, used to fit the cost model.",
+           "shape": shape, "calibration_seed": traces.CALIBRATION_SEED,
+           "device": torch.cuda.get_device_name(0), "calibration": calib,
+           "seconds": round(time.time() - t0, 1)}
+    out = args.out if args.out != engine.COST_MODEL_PATH else os.path.join(
+        os.path.dirname(engine.COST_MODEL_PATH),
+        f"cost_calib_hq{args.hq}_hkv{args.hkv}_{args.dtype}.json")
+    with open(out, "w") as f:
+        json.dump(doc, f, indent=1)
+    log(f"wrote {out}")
+    return 0
+
+
+def cmd_fit(args) -> int:
+    table, samples, sources = all_samples(args.table)
     w = fit(samples)
     rel = np.array([(float(w[p] @ f) - t) / t for _, _, p, f, t in samples])
     doc = {
         "about": "Learned cost model for MI355X: per-path linear model of the step time in "
                  "microseconds over the plan features of pkv_cost_features (include/pkv.h).",
-        "trained_on": {"table": "policy_table.json calibration timings",
-                       "seed": table["calibration_seed"], "samples": len(samples)},
+        "trained_on": {"files": sources, "seed": table["calibration_seed"],
+                       "samples": len(samples)},
         "num_cus": NUM_CUS,
         "ridge": RIDGE,
         "candidates": [{"path": p, "splits": s} for p, s in CANDIDATES],
@@ -182,6 +240,32 @@ def cmd_check(args) -> int:
                 f"table {t_path}:{t_s} {t_table:.2f} us, best single {best_single:.2f} us")
             del views, wd, w
             torch.cuda.empty_cache()
+    held["traces"] = {}
+    for name in TRACE_WORKLOADS:
+        spec = traces.get_spec(name)
+        w = traces.generate(spec, traces.HELD_OUT_SEED)
+        lens = w["seq_lens"].numpy()
+        m_path, m_s, pred = engine.choose_model(model, engine.problem_from_workload(w), lens)
+        t_path, t_s = engine.choose(rules, spec.batch, int(lens.max()))
+        singles = [(p, (1 if p == "nosplit" else spec.splits)) for p, _ in SINGLE_PATHS]
+        configs = list(dict.fromkeys(singles + [(t_path, t_s), (m_path, m_s)]))
+        wd = engine.to_device(w)
+        engine.validate_inputs(wd)
+        views = timing.pool_copies(wd, 1.0, max_copies=8)
+        times = timing.time_paths_interleaved(w, views, configs, "auto", args.steps,
+                                              args.warmup, repeats=7)
+        t_model, t_table = times[f"{m_path}:{m_s}"], times[f"{t_path}:{t_s}"]
+        best_single = min(times[f"{p}:{s}"] for p, s in singles)
+        held["traces"][name] = {
+            "n_max": int(lens.max()), "model": f"{m_path}:{m_s}", "model_predicted_us":
+            round(pred, 2), "table": f"{t_path}:{t_s}",
+            "times": {k: round(v, 2) for k, v in times.items()},
+            "model_over_best_single": round(t_model / best_single, 4),
+            "table_over_best_single": round(t_table / best_single, 4)}
+        log(f"  {name}: model {m_path}:{m_s} {t_model:.2f} us (predicted {pred:.2f}), "
+            f"table {t_path}:{t_s} {t_table:.2f} us, best single {best_single:.2f} us")
+        del views, wd, w
+        torch.cuda.empty_cache()
     doc["heldout"] = {"seed": traces.HELD_OUT_SEED, "device": torch.cuda.get_device_name(0),
                       "cells": held, "total_us": {k: round(v, 2) for k, v in totals.items()},
                       "seconds": round(time.time() - t0, 1)}
@@ -193,13 +277,16 @@ def cmd_check(args) -> int:
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("cmd", choices=("fit", "check"))
+    ap.add_argument("cmd", choices=("measure", "fit", "check"))
+    ap.add_argument("--hq", type=int, default=32)
+    ap.add_argument("--hkv", type=int, default=8)
+    ap.add_argument("--dtype", default="f16")
     ap.add_argument("--table", default=engine.POLICY_TABLE_PATH)
     ap.add_argument("--out", default=engine.COST_MODEL_PATH)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     args = ap.parse_args(argv)
-    return cmd_fit(args) if args.cmd == "fit" else cmd_check(args)
+    return {"measure": cmd_measure, "fit": cmd_fit, "check": cmd_check}[args.cmd](args)
 
 
 if __name__ == "__main__":
