@@ -77,6 +77,47 @@ def test_attention_matches_torch_sdpa_on_dense_kv(hq, hkv, d, lens, page_size):
                                    rtol=1e-12, atol=1e-12)
 
 
+def _brute_force_row_head(q, k_pool, v_pool, bt_row, n, h, group, scale, page_size):
+    """Scalar loops over Python floats: the decode definition, token by token."""
+    g = h // group
+    scores, vals = [], []
+    for t in range(n):
+        page, slot = int(bt_row[t // page_size]), t % page_size
+        k = [float(x) for x in k_pool[page, g, slot]]
+        v = [float(x) for x in v_pool[page, g, slot]]
+        scores.append(scale * sum(float(a) * b for a, b in zip(q[h], k)))
+        vals.append(v)
+    if n == 0:
+        return [0.0] * q.shape[-1], -math.inf
+    mx = max(scores)
+    w = [math.exp(x - mx) for x in scores]
+    den = sum(w)
+    out = [sum(w[t] * vals[t][j] for t in range(n)) / den for j in range(q.shape[-1])]
+    return out, mx + math.log(den)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_matches_scalar_brute_force_on_tiny_shapes(seed):
+    """B <= 3, N <= 40 with the page-boundary lengths, d = 8, P = 4."""
+    rng = np.random.default_rng(300 + seed)
+    b = int(rng.integers(1, 4))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 3]))
+    lens = [int(x) for x in rng.choice([0, 1, 3, 4, 5, 8, 9, 17, 40], size=b)]
+    q, _, _, k_pool, v_pool, bt = _random_case(rng, b, hq, hkv, 8, lens, 4)
+    scale = 1.0 / math.sqrt(8)
+    out, lse = attention(q, k_pool, v_pool, bt, np.array(lens), scale, 4, "f16")
+    for i, n in enumerate(lens):
+        for h in range(hq):
+            ref, ref_lse = _brute_force_row_head(q[i], k_pool, v_pool, bt[i], n, h, hq // hkv,
+                                                 scale, 4)
+            np.testing.assert_allclose(out[i, h], ref, rtol=1e-12, atol=1e-12)
+            if n == 0:
+                assert math.isinf(lse[i, h]) and lse[i, h] < 0
+            else:
+                assert abs(lse[i, h] - ref_lse) <= 1e-12 * max(1.0, abs(ref_lse))
+
+
 def test_golden_two_token_example():
     with open(os.path.join(GOLDEN, "two_token_example.json")) as f:
         g = json.load(f)
