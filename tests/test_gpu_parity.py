@@ -264,3 +264,21 @@ def test_random_small_problems_every_path(seed):
         step, _ = _run(w, path, 1 if path == "nosplit" else s, "auto")
         check_out(step.out, ref_out, dtype, label=f"random{seed}/{path}")
         check_lse(step.lse, ref_lse, label=f"random{seed}/{path}")
+
+
+def test_large_batch_short_contexts_every_path():
+    """512 rows of 1..600 tokens (G = 8, bf16): hundreds of exact buckets and
+    grids of tens of thousands of workgroups, on sampled rows."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 601, size=512).astype(np.int32)
+    lens[::97] = 0
+    spec = traces.custom_spec(512, 64, 8, 128, splits=8, dtype="bf16")
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    rows = sorted({0, 1, 97, 255, int(lens.argmax()), 510, 511})
+    say(f"[large batch] B=512 rows {rows}")
+    ref_out, ref_lse = oracle_out(w, rows=rows)
+    for path, s in (("workqueue", 8), ("bucketed", 8), ("padded", 8), ("nosplit", 1)):
+        step, _ = _run(w, path, s, "auto")
+        check_out(step.out, ref_out, "bf16", rows=rows, label=f"large/{path}")
+        check_lse(step.lse, ref_lse, rows=rows, label=f"large/{path}")
+        assert torch.isfinite(step.out.float()).all()
