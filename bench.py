@@ -1,7 +1,7 @@
 """Decode-attention benchmark: µs per decode step and achieved HBM GB/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
-                    [--path bucketed|workqueue|nosplit|padded|policy|model] [--kernel auto|valu|mfma]
+                    [--path bucketed|workqueue|nosplit|padded|policy|model|device] [--kernel auto|valu|mfma]
 
 One step is the engine's device work for one decode step of one layer: the
 split kernel launch(es) and the merge launch(es) (or the single no-split
@@ -216,6 +216,28 @@ def run_all(args) -> int:
     return 0
 
 
+def run_device(args, spec, seed, splits, w, wd, lens) -> int:
+    """The device-planned workqueue step (pkv_plan_device -> pkv_decode_device ->
+    pkv_merge_device, no host work): one JSON line of the same metric, without
+    the per-kernel roofline (the three launches are timed together)."""
+    from paged_kv_gqa_block_amd import timing
+
+    views = timing.pool_copies(wd, args.copies_gib)
+    r = timing.time_device_path(w, views, splits, args.steps, args.warmup, repeats=1)
+    kv = int(lens.astype("int64").sum()) * spec.num_kv_heads * spec.head_dim * 2 * 2
+    gbs = kv / (r["step_us"] * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "us_per_step": round(r["step_us"], 2),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "higher_is_better": True,
+        "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": describe(spec, "device-planned workqueue", splits, lens),
+                   "seed": seed, "path": "device", "splits": splits, "n_tasks": r["n_tasks"],
+                   "launches_per_step": 3, "kv_bytes": kv,
+                   "sync_wall_us": round(r["sync_wall_us_median"], 1)}}), flush=True)
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -244,6 +266,8 @@ def main(argv=None):
                                               engine.problem_from_workload(w), lens)
     wd = engine.to_device(w)
     engine.validate_inputs(wd)
+    if path == "device":
+        return run_device(args, spec, seed, splits, w, wd, lens)
 
     kernel_used = args.kernel
     if kernel_used == "auto":  # the library's AUTO rule: matrix cores for d = 128
