@@ -54,3 +54,8 @@ def test_recorded_heldout_check():
     for family in h["cells"].values():
         for rec in family.values():
             assert rec["model"] in rec["times"] and rec["table"] in rec["times"]
+            assert rec["model_over_best_single"] <= 1.10
+    # Summed over the sweep families the model is no slower than any single path.
+    totals = h["total_us"]
+    singles = [v for k, v in totals.items() if ":" in k]
+    assert totals["model"] <= min(singles)
