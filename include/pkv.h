@@ -195,10 +195,13 @@ size_t pkv_plan_bytes(const pkv_problem* prob, int32_t path, int32_t max_splits)
  *              ending at T_i; its grid has rows_b * Hkv * S slots, the rest
  *              neutral.
  *   NOSPLIT:   one task per (row, kv head) of every non-empty row.
+ * The whole buffer of pkv_plan_bytes bytes is working memory: bucketed and
+ * padded plans order their rows in its last B words before moving the order
+ * into place, so words past the used length are unspecified afterwards.
  * Errors: PKV_EINVAL (null pointer, max_splits < 1 or > 65535, bad path),
- * PKV_ESHAPE (problem shape), PKV_ERANGE (N_i < 0 or N_i > max_pages_per_row*P),
- * PKV_ENOSPC (plan_bytes too small), PKV_EHIP (the copy failed to enqueue).
- * info_out may be NULL.
+ * PKV_ESHAPE (problem shape), PKV_ERANGE (N_i < 0 or N_i > max_pages_per_row*P,
+ * or more than 2^31 - 1 tasks or state slots), PKV_ENOSPC (plan_bytes too
+ * small), PKV_EHIP (the copy failed to enqueue).  info_out may be NULL.
  */
 pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_host, int32_t path,
                     int32_t max_splits, void* plan_host, void* plan_dev, size_t plan_bytes,
