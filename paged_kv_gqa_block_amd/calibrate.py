@@ -113,11 +113,17 @@ def main(argv=None):
     ap.add_argument("--out", default=engine.POLICY_TABLE_PATH)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rules-from", default=None,
+                    help="reuse the calibration timings of this table; rebuild the rules "
+                         "and rerun only the held-out check")
     args = ap.parse_args(argv)
     assert torch.cuda.is_available(), "calibration needs a GPU"
     t0 = time.time()
     calib, held = {}, {}
-    for b in traces.POLICY_BATCHES:
+    if args.rules_from:
+        with open(args.rules_from) as f:
+            calib = json.load(f)["calibration"]
+    for b in ([] if args.rules_from else traces.POLICY_BATCHES):
         for n in grid_of(b):
             n_max, times = measure(cell_spec(b, n), traces.CALIBRATION_SEED, CANDIDATES,
                                    args.steps, args.warmup)
