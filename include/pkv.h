@@ -32,7 +32,9 @@
  *     re-entrant.
  *   - Streams: GPU work is enqueued asynchronously on the given stream; the
  *     library never synchronises.  A NULL stream is the default stream.
- *   - Errors: a negative pkv_status is returned and nothing is enqueued.
+ *   - Errors: a negative pkv_status is returned and nothing is enqueued,
+ *     except for PKV_EHIP from a launch that failed after earlier launches
+ *     of the same call (bucketed and padded plans launch once per bucket).
  *     Arguments are validated on the host before any launch.  Block-table
  *     entries are not read on the host: an entry outside [0, num_pool_pages)
  *     among a row's first ceil(N_i / P) entries is undefined behaviour.
@@ -200,7 +202,7 @@ size_t pkv_plan_bytes(const pkv_problem* prob, int32_t path, int32_t max_splits)
  * into place, so words past the used length are unspecified afterwards.
  * Errors: PKV_EINVAL (null pointer, max_splits < 1 or > 65535, bad path),
  * PKV_ESHAPE (problem shape), PKV_ERANGE (N_i < 0 or N_i > max_pages_per_row*P,
- * or more than 2^31 - 1 tasks or state slots), PKV_ENOSPC (plan_bytes too
+ * or more than 2^31 - 1 tasks, state slots or plan words), PKV_ENOSPC (plan_bytes too
  * small), PKV_EHIP (the copy failed to enqueue).  info_out may be NULL.
  */
 pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_host, int32_t path,
@@ -222,7 +224,8 @@ pkv_status pkv_plan_get_info(const pkv_problem* prob, const void* plan_host,
  * Tokens past N_i in a row's last page, and pool pages not referenced by the
  * first T_i table entries of a row, are never used (they may hold NaN).
  * Errors: PKV_EINVAL, PKV_ESHAPE (shape or plan/problem mismatch),
- * PKV_EDTYPE, PKV_EHIP.
+ * PKV_EDTYPE, PKV_ERANGE (a launch of more than 2^24 - 1 workgroups: tasks,
+ * B * Hkv for NOSPLIT, or rows_b * Hkv * S for one bucket), PKV_EHIP.
  */
 pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host, const void* plan_dev,
                       const void* q, const void* k_pool, const void* v_pool,
@@ -236,7 +239,8 @@ pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host, const void
  * problem dtype, lse = M + ln L.  All-neutral rows give out = 0, lse = -inf.
  * WORKQUEUE: one launch; BUCKETED / PADDED: one launch per bucket;
  * NOSPLIT: no-op.
- * lse may be NULL.  Errors as pkv_decode.
+ * lse may be NULL.  Errors as pkv_decode; PKV_ERANGE when a launch's rows
+ * times Hq exceed 2^24 - 1 workgroups.
  */
 pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void* plan_dev,
                      const float* st_m, const float* st_l, const float* st_o, void* out,
@@ -333,7 +337,8 @@ pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan_dev, const
  * A negative position marks an inactive row; positions at or past
  * max_pages_per_row * P are skipped.  The block-table entry of the written
  * page must be a valid pool page (undefined behaviour otherwise, as for
- * pkv_decode).  Errors: PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_EHIP.
+ * pkv_decode).  Errors: PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE
+ * (B * Hkv above 2^24 - 1), PKV_EHIP.
  */
 pkv_status pkv_append_kv(const pkv_problem* prob, const void* k_new, const void* v_new,
                          const int32_t* block_table, const int32_t* positions_dev, void* k_pool,

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "launch_limits.h"
 #include "pkv_internal.h"
 
 using namespace pkv;
@@ -78,24 +79,28 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
   if (path == PKV_WORKQUEUE) {
     const int n = w[kNumTasks];
     if (n == 0) return PKV_OK;
+    if (n > kMaxGridGroups) return PKV_ERANGE;
     a.tasks = dev + w[kOffTasks];
     a.num_items = n;
     return launch_split(*prob, kModeWorkqueue, prob->kernel, a, n, stream);
   }
   if (path == PKV_NOSPLIT) {
-    const int n = prob->batch * prob->num_kv_heads;
-    a.num_items = n;
-    return launch_split(*prob, kModeNoSplit, prob->kernel, a, n, stream);
+    const int64_t n = int64_t(prob->batch) * prob->num_kv_heads;
+    if (n > kMaxGridGroups) return PKV_ERANGE;
+    a.num_items = static_cast<int32_t>(n);
+    return launch_split(*prob, kModeNoSplit, prob->kernel, a, static_cast<int>(n), stream);
   }
   // BUCKETED / PADDED: one rectangular rows_b x Hkv x S launch per bucket.
   // Rows of a padded bucket differ in length: the kernel takes each row's
   // length from the plan's row_len array (bucket length word -1).
   a.row_len = dev + PKV_PLAN_HEADER_WORDS;
   const int32_t* bw = w + w[kOffBuckets];
+  for (int k = 0; k < w[kNumBuckets]; ++k)  // every launch size, before the first launch
+    if (int64_t(bw[kBucketWords * k + 4]) * prob->num_kv_heads * w[kSplits] > kMaxGridGroups)
+      return PKV_ERANGE;
   for (int k = 0; k < w[kNumBuckets]; ++k) {
     const int32_t* e = bw + kBucketWords * k;
     const int64_t items = int64_t(e[4]) * prob->num_kv_heads * w[kSplits];
-    if (items > INT32_MAX) return PKV_ERANGE;
     a.bucket_len = e[0];
     a.bucket_pages = e[1];
     a.bucket_pps = e[2];
@@ -123,6 +128,8 @@ extern "C" pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host,
   if (w[kNumStateSlots] > 0 && (!st_m || !st_l || !st_o)) return PKV_EINVAL;
   const int32_t* dev = static_cast<const int32_t*>(plan_dev);
   const int b = prob->batch;
+  // One launch covers at most B rows x Hq heads (workqueue: exactly that).
+  if (int64_t(b) * prob->num_q_heads > kMaxGridGroups) return PKV_ERANGE;
 
   MergeArgs a{};
   a.st_m = st_m;

@@ -11,6 +11,7 @@
 // lanes 32..32+d/8-1 the value, 16 bytes each.  Rows with a negative position
 // are inactive; positions at or past the block table's capacity are skipped.
 #include "device_common.h"
+#include "launch_limits.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -37,9 +38,10 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 }  // namespace
 
 pkv_status launch_append(const AppendArgs& a, int batch, hipStream_t s) {
-  const int grid = batch * a.num_kv_heads;
+  const int64_t grid = int64_t(batch) * a.num_kv_heads;
   if (grid <= 0) return PKV_OK;
-  hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(64), 0, s, a);
+  if (grid > kMaxGridGroups) return PKV_ERANGE;
+  hipLaunchKernelGGL(append_kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0, s, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

@@ -14,6 +14,7 @@
 // issued up front.  Each thread keeps an online-rescaled partial (max, sum,
 // 4 outputs); split groups are then combined through LDS.
 #include "device_common.h"
+#include "launch_limits.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -125,9 +126,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }  // namespace
 
 pkv_status launch_merge(const pkv_problem& p, const MergeArgs& a, hipStream_t s) {
-  const int items = a.num_rows * p.num_q_heads;
+  const int64_t items = int64_t(a.num_rows) * p.num_q_heads;
   if (items == 0) return PKV_OK;
-  const dim3 grid(items), block(256);
+  if (items > kMaxGridGroups) return PKV_ERANGE;
+  const dim3 grid(static_cast<uint32_t>(items)), block(256);
   const bool bf = p.dtype == PKV_BF16;
   if (p.head_dim == 128) {
     if (bf) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, s, a);

@@ -161,6 +161,7 @@ extern "C" pkv_status pkv_plan(const pkv_problem* prob, const int32_t* seq_lens_
   const int64_t off_buckets = off_tasks + kTaskWords * c.n_tasks;
   const int64_t off_brows = off_buckets + kBucketWords * int64_t(c.n_buckets);
   const int64_t total = off_brows + (bucketed ? b : 0);
+  if (total > INT32_MAX) return PKV_ERANGE;  // header offsets are 32-bit words
   if (bucketed) {
     std::memmove(w + off_brows, order, size_t(b) * sizeof(int32_t));
     order = w + off_brows;  // tasks and buckets are written below this point

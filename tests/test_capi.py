@@ -216,6 +216,38 @@ def test_decode_and_merge_validate_before_launch():
     assert e.value.status == PKV_EDTYPE
 
 
+def test_launches_past_the_dispatch_limit_are_rejected_before_launch():
+    """A launch's work-item count (workgroups x threads) must fit 32 bits; the
+    library rejects grids of more than 2^24 - 1 workgroups with ERANGE before
+    enqueuing anything.  Lengths are zero or one page, so the plans touch
+    little memory (np.zeros pages are allocated lazily)."""
+    fake = 0x1000  # never dereferenced: every call below fails validation first
+    limit = (1 << 24) - 1
+    # Merge: B x Hq workgroups.
+    prob = _prob(65536, hq=256, hkv=16, max_pages=4)
+    assert 65536 * 256 > limit
+    buf = _plan_buf(prob, np.zeros(65536, np.int32), PKV_WORKQUEUE, 1)
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_merge(prob, buf, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ERANGE
+    # No-split decode: B x Hkv workgroups; append: the same grid.
+    prob = _prob(1 << 20, hq=16, hkv=16, max_pages=4)
+    buf = _plan_buf(prob, np.zeros(1 << 20, np.int32), PKV_NOSPLIT, 1)
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_decode(prob, buf, fake, fake, fake, fake, fake, fake, None, None, None, fake)
+    assert e.value.status == PKV_ERANGE
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_append_kv(prob, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ERANGE
+    # Bucketed decode: rows_b x Hkv x S slots in one bucket's launch.
+    prob = _prob(32, hq=16, hkv=16, max_pages=4)
+    assert 32 * 16 * 65535 > limit
+    buf = _plan_buf(prob, np.full(32, 16, np.int32), PKV_BUCKETED, 65535)
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_decode(prob, buf, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ERANGE
+
+
 def test_status_strings():
     for s in range(-6, 1):
         assert _lib.pkv_status_str(s)
