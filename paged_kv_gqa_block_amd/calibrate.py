@@ -48,19 +48,21 @@ def log(*a):
 
 
 def cell_spec(batch: int, cap: int, num_q_heads: int | None = None,
-              num_kv_heads: int | None = None, dtype: str | None = None) -> traces.WorkloadSpec:
+              num_kv_heads: int | None = None, dtype: str | None = None,
+              head_dim: int | None = None) -> traces.WorkloadSpec:
     """Calibration workload of batch size `batch` with longest length `cap`
-    (head shape and dtype of the sweep unless given; the lengths depend only
-    on batch, cap and seed)."""
+    (head shape, head size and dtype of the sweep unless given; the lengths
+    depend only on batch, cap and seed)."""
     base = traces.get_spec(f"policy_b{batch}")
     hq = num_q_heads or base.num_q_heads
     hkv = num_kv_heads or base.num_kv_heads
     dt = dtype or base.dtype
+    d = head_dim or base.head_dim
     if batch == 1:
-        return traces.WorkloadSpec(f"cal_b1_n{cap}", 1, hq, hkv, base.head_dim, base.page_size,
+        return traces.WorkloadSpec(f"cal_b1_n{cap}", 1, hq, hkv, d, base.page_size,
                                    "fixed", base.splits, dt, fixed_len=cap)
     lo = 64 if cap <= 2048 else 1024
-    return traces.WorkloadSpec(f"cal_b{batch}_h{cap}", batch, hq, hkv, base.head_dim,
+    return traces.WorkloadSpec(f"cal_b{batch}_h{cap}", batch, hq, hkv, d,
                                base.page_size, "uniform", base.splits, dt, lo=lo, hi=cap)
 
 

@@ -4,6 +4,11 @@
                                                       # GPU: calibration timings, another shape
     python -m paged_kv_gqa_block_amd.cost_fit fit     # CPU: from stored calibration timings
     python -m paged_kv_gqa_block_amd.cost_fit check   # GPU: held-out measurement
+    python -m paged_kv_gqa_block_amd.cost_fit measure --hq 32 --hkv 2 --seed 20260623
+                                                      # GPU: held-out timings, another shape
+    python -m paged_kv_gqa_block_amd.cost_fit evaluate cost_heldout_*.json
+                                                      # CPU: the model's and the table's
+                                                      #      choices on stored timings
 
 The PersistentKV summary pages leave a learned cost model as future work
 ("Conclusion").  Here the model is one linear function per path of the plan
@@ -22,7 +27,11 @@ another head shape / dtype and stores them beside the table
 (cost_calib_*.json); `fit` uses every such file too.  `check` measures, on
 held-out seed 20260623, the model's choice beside the table's choice and the
 four single paths, with interleaved repeats: on the two sweep families and on
-the trace workloads (another head shape and dtype).
+the trace workloads (another head shape and dtype).  `measure --seed
+20260623` stores held-out timings of every candidate for a head shape
+(cost_heldout_*.json, which `fit` does not read), and `evaluate` scores the
+model's and the table's choices on such files: a check at head shapes and
+head sizes the model was not trained on.
 """
 from __future__ import annotations
 
@@ -51,15 +60,29 @@ def sweep_problem(batch: int, shape: dict | None = None) -> _lib.pkv_problem:
     base = traces.get_spec(f"policy_b{batch}")
     shape = shape or {}
     return _lib.make_problem(batch, shape.get("num_q_heads", base.num_q_heads),
-                             shape.get("num_kv_heads", base.num_kv_heads), base.head_dim,
+                             shape.get("num_kv_heads", base.num_kv_heads),
+                             shape.get("head_dim", base.head_dim),
                              base.page_size, 1 << 20, 32768 // base.page_size,
                              shape.get("dtype", base.dtype))
+
+
+def shape_tag(shape: dict | None) -> str:
+    if not shape:
+        return ""
+    d = shape.get("head_dim", 128)
+    return (f"{shape['num_q_heads']}/{shape['num_kv_heads']}/{shape['dtype']}"
+            + (f"/d{d}" if d != 128 else "") + ":")
+
+
+def shape_of(key: str) -> str:
+    """The shape tag of a cell key ("" for the sweep's own shape)."""
+    return ":".join(key.split(":")[:-2])
 
 
 def samples_from_table(table: dict, shape: dict | None = None):
     """(cell, candidate, path, features, us) of every calibration timing."""
     out = []
-    tag = "" if not shape else f"{shape['num_q_heads']}/{shape['num_kv_heads']}/{shape['dtype']}:"
+    tag = shape_tag(shape)
     for key, cell in table["calibration"].items():
         b, cap = cell["batch"], cell["cap"]
         lens = traces.draw_lengths(cell_spec(b, cap),
@@ -118,8 +141,8 @@ def cross_validate(samples) -> dict:
                           [{c for c in cells if c.split(":")[-2] == str(b)}
                            for b in traces.POLICY_BATCHES]),
                          ("leave_one_shape_out",
-                          [{c for c in cells if c.count(":") == 1},
-                           {c for c in cells if c.count(":") > 1}])):
+                          [{c for c in cells if shape_of(c) == t}
+                           for t in sorted({shape_of(c) for c in cells})])):
         if any(not g for g in groups) or len(groups) < 2:
             continue
         tot = {"model_total_us": 0.0, "best_total_us": 0.0, "cells_over_3pct": 0}
@@ -151,22 +174,27 @@ def cmd_measure(args) -> int:
     import torch
 
     assert torch.cuda.is_available(), "measuring needs a GPU"
-    shape = {"num_q_heads": args.hq, "num_kv_heads": args.hkv, "dtype": args.dtype}
+    shape = {"num_q_heads": args.hq, "num_kv_heads": args.hkv, "dtype": args.dtype,
+             "head_dim": args.d}
     calib = {}
     t0 = time.time()
     for b in traces.POLICY_BATCHES:
         for n in grid_of(b):
-            n_max, times = measure(cell_spec(b, n, args.hq, args.hkv, args.dtype),
-                                   traces.CALIBRATION_SEED, CANDIDATES, args.steps, args.warmup)
+            n_max, times = measure(cell_spec(b, n, args.hq, args.hkv, args.dtype, args.d),
+                                   args.seed, CANDIDATES, args.steps, args.warmup)
             calib[f"{b}:{n}"] = {"batch": b, "cap": n, "n_max": n_max, "times": times}
-    doc = {"about": "Calibration timings of every candidate path on the (B, N_max) grid for "
-                    "one head shape, used to fit the cost model.",
-           "shape": shape, "calibration_seed": traces.CALIBRATION_SEED,
+    held_out = args.seed != traces.CALIBRATION_SEED
+    doc = {"about": ("Held-out timings of every candidate path on the (B, N_max) grid for one "
+                     "head shape, used to check the cost model (not to fit it)." if held_out else
+                     "Calibration timings of every candidate path on the (B, N_max) grid for "
+                     "one head shape, used to fit the cost model."),
+           "shape": shape, "calibration_seed": args.seed,
            "device": torch.cuda.get_device_name(0), "calibration": calib,
            "seconds": round(time.time() - t0, 1)}
+    stem = (f"hq{args.hq}_hkv{args.hkv}_{args.dtype}" + (f"_d{args.d}" if args.d != 128 else ""))
+    name = f"cost_heldout_{stem}.json" if held_out else f"cost_calib_{stem}.json"
     out = args.out if args.out != engine.COST_MODEL_PATH else os.path.join(
-        os.path.dirname(engine.COST_MODEL_PATH),
-        f"cost_calib_hq{args.hq}_hkv{args.hkv}_{args.dtype}.json")
+        os.path.dirname(engine.COST_MODEL_PATH), name)
     with open(out, "w") as f:
         json.dump(doc, f, indent=1)
     log(f"wrote {out}")
@@ -275,18 +303,67 @@ def cmd_check(args) -> int:
     return 0
 
 
+def evaluate_file(path: str, model_path: str) -> dict:
+    """The model's and the table's choices against the best candidate and the
+    best single path, on the stored timings of one file (any shape, any seed)."""
+    with open(path) as f:
+        doc = json.load(f)
+    shape = doc["shape"]
+    model = engine.load_cost_model(model_path)
+    rules = engine.load_policy_table()
+    tot = {"model": 0.0, "table": 0.0, "best": 0.0, **{f"{p}:{s}": 0.0 for p, s in SINGLE_PATHS}}
+    worse = {"model": 0, "table": 0}
+    for cell in doc["calibration"].values():
+        b, cap, times = cell["batch"], cell["cap"], cell["times"]
+        lens = traces.draw_lengths(cell_spec(b, cap), np.random.default_rng(doc["calibration_seed"]))
+        if int(lens.max()) != cell["n_max"]:
+            raise RuntimeError(f"{path}: regenerated lengths differ from the measured ones")
+        m_path, m_s, _ = engine.choose_model(model, sweep_problem(b, shape), lens)
+        t_path, t_s = engine.choose(rules, b, int(lens.max()))
+        best = min(times.values())
+        for who, key in (("model", f"{m_path}:{m_s}"), ("table", f"{t_path}:{t_s}")):
+            tot[who] += times[key]
+            worse[who] += times[key] > best * (1 + NOISE)
+        tot["best"] += best
+        for p, s in SINGLE_PATHS:
+            tot[f"{p}:{s}"] += times[f"{p}:{s}"]
+    return {"file": os.path.basename(path), "shape": shape, "seed": doc["calibration_seed"],
+            "cells": len(doc["calibration"]),
+            "total_us": {k: round(v, 2) for k, v in tot.items()},
+            "model_over_best": round(tot["model"] / tot["best"] - 1, 4),
+            "table_over_best": round(tot["table"] / tot["best"] - 1, 4),
+            "cells_over_3pct": worse}
+
+
+def cmd_evaluate(args) -> int:
+    with open(args.out) as f:
+        doc = json.load(f)
+    res = [evaluate_file(p, args.out) for p in args.files]
+    for r in res:
+        log(json.dumps(r))
+    doc["shape_checks"] = {r["file"]: r for r in res}
+    with open(args.out, "w") as f:
+        json.dump(doc, f, indent=1)
+    log(f"wrote {args.out}")
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("cmd", choices=("measure", "fit", "check"))
+    ap.add_argument("cmd", choices=("measure", "fit", "check", "evaluate"))
+    ap.add_argument("files", nargs="*", help="evaluate: timing files (cost_*.json)")
     ap.add_argument("--hq", type=int, default=32)
     ap.add_argument("--hkv", type=int, default=8)
+    ap.add_argument("--d", type=int, default=128)
+    ap.add_argument("--seed", type=int, default=traces.CALIBRATION_SEED)
     ap.add_argument("--dtype", default="f16")
     ap.add_argument("--table", default=engine.POLICY_TABLE_PATH)
     ap.add_argument("--out", default=engine.COST_MODEL_PATH)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     args = ap.parse_args(argv)
-    return {"measure": cmd_measure, "fit": cmd_fit, "check": cmd_check}[args.cmd](args)
+    return {"measure": cmd_measure, "fit": cmd_fit, "check": cmd_check,
+            "evaluate": cmd_evaluate}[args.cmd](args)
 
 
 if __name__ == "__main__":

@@ -146,6 +146,12 @@ extern "C" pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host,
     a.num_rows = b;
     a.mode = kModeWorkqueue;
     a.bucket_row0 = -1;
+    // When all rows share one split count, the merge derives each row's
+    // first state slot from the row index (read from the host plan here).
+    const int32_t* ns = w + PKV_PLAN_HEADER_WORDS + 2 * b;
+    a.uniform_nsplit = ns[0];
+    for (int r = 1; r < b && a.uniform_nsplit > 0; ++r)
+      if (ns[r] != a.uniform_nsplit) a.uniform_nsplit = 0;
     return launch_merge(*prob, a, stream);
   }
   const int32_t* bw = w + w[kOffBuckets];

@@ -37,7 +37,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int hh = h - g * G;
   int row, nsplit;
   int64_t base;  // first state slot of this (row, kv head)
-  if (a.mode == kModeWorkqueue) {
+  if (a.mode == kModeWorkqueue && a.uniform_nsplit > 0) {
+    // Every row has the same split count, so the row's first slot follows
+    // from its index and the plan's row arrays need not be read (one
+    // dependent memory round trip less).
+    row = ri;
+    nsplit = a.uniform_nsplit;
+    base = (int64_t(row) * hkv + g) * nsplit;
+  } else if (a.mode == kModeWorkqueue) {
     row = ri;
     nsplit = a.row_nsplit[row];
     base = int64_t(a.row_task_off[row]) + int64_t(g) * nsplit;

@@ -141,6 +141,7 @@ struct MergeArgs {
   int32_t mode;       // kModeWorkqueue or kModeBucket
   int32_t bucket_row0;  // bucket: its only row when it has one, else -1
   int32_t* device_plan;  // device-planned step: the merge resets its work counter; else null
+  int32_t uniform_nsplit;  // workqueue: the split count every row shares (> 0), else 0
 };
 
 struct AppendArgs {

@@ -266,6 +266,25 @@ def test_random_small_problems_every_path(seed):
         check_lse(step.lse, ref_lse, label=f"random{seed}/{path}")
 
 
+@pytest.mark.parametrize("lens", ([500, 510, 497, 512],    # equal page counts
+                                  [481, 512, 465, 450],    # equal split counts, unequal pages
+                                  [481, 512, 0, 450],      # an empty row: counts differ
+                                  [481, 512, 40, 450]))    # a short row: counts differ
+def test_workqueue_merge_with_shared_and_mixed_split_counts(lens):
+    """The workqueue merge locates a row's states from its index when every
+    row has the same split count, and from the plan's row arrays otherwise:
+    both against the oracle, on both kernels' states."""
+    lens = np.asarray(lens, dtype=np.int32)
+    spec = traces.custom_spec(4, 32, 8, 128, splits=8, dtype="f16")
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    say(f"[wq merge] lens={lens.tolist()}")
+    ref_out, ref_lse = oracle_out(w)
+    for kernel in KERNELS:
+        step, _ = _run(w, "workqueue", 8, kernel)
+        check_out(step.out, ref_out, "f16", label=f"wqmerge/{kernel}")
+        check_lse(step.lse, ref_lse, label=f"wqmerge/{kernel}")
+
+
 def test_large_batch_short_contexts_every_path():
     """512 rows of 1..600 tokens (G = 8, bf16): hundreds of exact buckets and
     grids of tens of thousands of workgroups, on sampled rows."""
