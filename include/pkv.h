@@ -107,7 +107,8 @@ typedef struct pkv_problem {
   int32_t head_dim;          /* d: 64 or 128                                  */
   int32_t page_size;         /* P: 16 tokens per page                         */
   int32_t num_pool_pages;    /* pages in each of the K and V pools, >= 1      */
-  int32_t max_pages_per_row; /* block-table row stride, >= 1                  */
+  int32_t max_pages_per_row; /* block-table row stride, 1 .. 2^27 - 1 (token
+                                indices stay within 32 bits)                 */
   int32_t dtype;             /* PKV_F16 or PKV_BF16 (q, pools and out)        */
   float sm_scale;            /* softmax scale, e.g. 1/sqrt(d)                 */
   int32_t kernel;            /* PKV_KERNEL_*                                  */

@@ -29,6 +29,9 @@ pkv_status check_problem(const pkv_problem* p) {
   if (p->num_q_heads % p->num_kv_heads != 0) return PKV_ESHAPE;
   if (p->num_q_heads / p->num_kv_heads > kMaxGroup) return PKV_ESHAPE;
   if (p->num_kv_heads > 32767) return PKV_ESHAPE;
+  // Token indices (up to max_pages_per_row * 16, plus 15 when rounding up to
+  // pages) are 32-bit in the kernels.
+  if (p->max_pages_per_row > INT32_MAX / kPageSize) return PKV_ESHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return PKV_ESHAPE;
   if (p->page_size != kPageSize) return PKV_ESHAPE;
   if (p->dtype != PKV_F16 && p->dtype != PKV_BF16) return PKV_EDTYPE;

@@ -143,6 +143,7 @@ def test_policy_errors():
     ("batch", 0, PKV_EINVAL),
     ("kernel", 9, PKV_EINVAL),
     ("num_pool_pages", 0, PKV_EINVAL),
+    ("max_pages_per_row", 1 << 27, PKV_ESHAPE),  # token indices past 32 bits
 ])
 def test_plan_rejects_bad_problems(field, value, status):
     prob = _prob(2)
