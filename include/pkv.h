@@ -297,8 +297,9 @@ pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_model* model
  * pkv_plan_device builds the WORKQUEUE plan on the GPU from the device copy
  * of the row lengths, in the same layout (and with the same contents, for
  * valid lengths) as pkv_plan(..., PKV_WORKQUEUE, ...).  plan_bytes must be at
- * least pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits); batch <= 16384
- * (else PKV_ERANGE).  Lengths cannot be
+ * least pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits); batch <= 16384,
+ * and that size in 32-bit words at most 2^31 - 1 (else PKV_ERANGE).
+ * Lengths cannot be
  * checked on the host: a row whose length lies outside
  * [0, max_pages_per_row * P] is planned as an empty row, and the number of
  * such rows is written to *bad_rows_dev when it is not NULL.

@@ -185,7 +185,11 @@ extern "C" pkv_status pkv_plan_device(const pkv_problem* prob, const int32_t* se
   if (!seq_lens_dev || !plan_dev) return PKV_EINVAL;
   if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
   if (prob->batch > kMaxDevicePlanRows) return PKV_ERANGE;
-  if (plan_bytes < pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits)) return PKV_ENOSPC;
+  // The kernel counts tasks and plan words in 32 bits: bound them by the
+  // largest plan this problem can have (every row at its full split count).
+  const size_t need = pkv_plan_bytes(prob, PKV_WORKQUEUE, max_splits);
+  if (need / sizeof(int32_t) > size_t(INT32_MAX)) return PKV_ERANGE;
+  if (plan_bytes < need) return PKV_ENOSPC;
   return launch_plan_device(*prob, seq_lens_dev, max_splits, static_cast<int32_t*>(plan_dev),
                             bad_rows_dev, stream);
 }

@@ -272,6 +272,12 @@ def test_device_plan_entry_points_validate_before_launch():
     with pytest.raises(PkvError) as e:
         _lib.pkv_plan_device(big, fake, 8, fake, _lib.pkv_plan_bytes(big, PKV_WORKQUEUE, 8))
     assert e.value.status == PKV_ERANGE
+    wide = _prob(16384, hq=4096, hkv=4096)  # a plan of more than 2^31 - 1 words
+    need = _lib.pkv_plan_bytes(wide, PKV_WORKQUEUE, 64)
+    assert need // 4 > 2**31 - 1
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_plan_device(wide, fake, 64, fake, need)
+    assert e.value.status == PKV_ERANGE
     with pytest.raises(PkvError) as e:  # d = 64 has no persistent kernel
         _lib.pkv_decode_device(_prob(2, d=64), fake, 8, fake, fake, fake, fake, fake, fake, fake)
     assert e.value.status == PKV_ESHAPE
