@@ -266,6 +266,10 @@ pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void*
  * time in microseconds as sum_j weights[path][j] * f_j.  pkv_policy_model
  * returns the candidate with the smallest prediction (the first one on a
  * tie) and, when predicted_us_out is not NULL, that prediction.
+ * The weights hold for one split kernel: the caller passes the weights fitted
+ * for the kernel pkv_decode will run on this problem (the shipped model has
+ * one set for the matrix-core kernel at G <= 8, one for its G > 8 variant
+ * and one for the vector-ALU kernel).
  * num_cus (1..1024): the device's compute units the model was fitted with.
  * scratch_host: B int32 of caller memory, used for bucket orders (may be
  * NULL when no candidate is BUCKETED or PADDED).  NOSPLIT candidates ignore

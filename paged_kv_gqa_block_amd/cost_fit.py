@@ -11,20 +11,21 @@
                                                       #      choices on stored timings
 
 The PersistentKV summary pages leave a learned cost model as future work
-("Conclusion").  Here the model is one linear function per path of the plan
-features of include/pkv.h (pkv_cost_features: launches, KV and state
-megabytes, per-CU critical pages, grid items, tasks), predicting the step time
-in microseconds.  `fit` takes the calibration timings stored in
+("Conclusion").  Here the model is, for each split kernel (matrix-core or
+vector-ALU) and each path, one linear function of the plan features of
+include/pkv.h (pkv_cost_features: launches, KV and state megabytes, per-CU
+critical pages, grid items, tasks), predicting the step time in
+microseconds.  `fit` takes the calibration timings stored in
 policy_table.json (every candidate path and split cap timed on seed 20260622
 over the (B, N_max) grid), regenerates each cell's lengths from the same seed,
 computes the features through the C ABI, and solves one least-squares problem
-per path on the relative error (each row scaled by 1 / measured time),
-with a small ridge term.  It also
-reports how the model's choices compare with the measured best, in sample,
-under 5-fold cross-validation over cells and leaving one batch size out.
-`measure` times the same candidates on the same (B, N_max) grid and seed for
-another head shape / dtype and stores them beside the table
-(cost_calib_*.json); `fit` uses every such file too.  `check` measures, on
+per (split kernel, path) on the relative error (each row scaled by 1 /
+measured time), with a small ridge term.  It also reports how the model's
+choices compare with the measured best, in sample, under 5-fold
+cross-validation over cells, leaving one batch size out and leaving one head
+shape out.  `measure` times the same candidates on the same (B, N_max) grid
+and seed for another head shape, head size or dtype and stores them beside
+the table (cost_calib_*.json); `fit` uses every such file too.  `check` measures, on
 held-out seed 20260623, the model's choice beside the table's choice and the
 four single paths, with interleaved repeats: on the two sweep families and on
 the trace workloads (another head shape and dtype).  `measure --seed
@@ -77,6 +78,22 @@ def shape_tag(shape: dict | None) -> str:
 def shape_of(key: str) -> str:
     """The shape tag of a cell key ("" for the sweep's own shape)."""
     return ":".join(key.split(":")[:-2])
+
+
+def kernel_of(key: str) -> str:
+    """The split-kernel variant that ran a cell (engine.split_kernel_of): the
+    vector-ALU kernel for d = 64 (head-size mark in the tag), else the
+    matrix-core kernel for G <= 8 or its G = 16 variant."""
+    tag = shape_of(key)
+    if "/d" in tag:
+        return "valu"
+    if not tag:
+        return "mfma"  # the sweep's own shape, 64/8
+    hq, hkv = (int(x) for x in tag.split("/")[:2])
+    return "mfma" if hq // hkv <= 8 else "mfma_g16"
+
+
+KERNELS = ("mfma", "mfma_g16", "valu")
 
 
 def samples_from_table(table: dict, shape: dict | None = None):
@@ -203,19 +220,29 @@ def cmd_measure(args) -> int:
 
 def cmd_fit(args) -> int:
     table, samples, sources = all_samples(args.table)
-    w = fit(samples)
-    rel = np.array([(float(w[p] @ f) - t) / t for _, _, p, f, t in samples])
+    weights, stats = {}, {}
+    for kernel in KERNELS:  # one model per split kernel: their costs per page differ
+        ss = [s for s in samples if kernel_of(s[0]) == kernel]
+        if not ss:
+            continue
+        w = fit(ss)
+        rel = np.array([(float(w[p] @ f) - t) / t for _, _, p, f, t in ss])
+        weights[kernel] = {p: [float(v) for v in w[p]] for p in PATHS}
+        stats[kernel] = {"samples": len(ss), "shapes": sorted({shape_of(s[0]) or "sweep"
+                                                               for s in ss}),
+                         "rms_relative_error": round(float(np.sqrt(np.mean(rel ** 2))), 4),
+                         "in_sample": choice_quality(w, ss), **cross_validate(ss)}
     doc = {
-        "about": "Learned cost model for MI355X: per-path linear model of the step time in "
-                 "microseconds over the plan features of pkv_cost_features (include/pkv.h).",
+        "about": "Learned cost model for MI355X: per split kernel and per path, a linear model "
+                 "of the step time in microseconds over the plan features of "
+                 "pkv_cost_features (include/pkv.h).",
         "trained_on": {"files": sources, "seed": table["calibration_seed"],
                        "samples": len(samples)},
         "num_cus": NUM_CUS,
         "ridge": RIDGE,
         "candidates": [{"path": p, "splits": s} for p, s in CANDIDATES],
-        "weights": {p: [float(v) for v in w[p]] for p in PATHS},
-        "fit": {"rms_relative_error": round(float(np.sqrt(np.mean(rel ** 2))), 4),
-                "in_sample": choice_quality(w, samples), **cross_validate(samples)},
+        "weights": weights,
+        "fit": stats,
     }
     with open(args.out, "w") as f:
         json.dump(doc, f, indent=1)

@@ -139,22 +139,39 @@ def choose(rules, batch: int, max_len: int):
     return PATH_NAMES[path], splits
 
 
+def split_kernel_of(prob: _lib.pkv_problem) -> str:
+    """The split-kernel variant pkv_decode runs for this problem: the explicit
+    choice, else the library's AUTO rule (matrix cores for d = 128, vector ALU
+    for 64).  The matrix-core kernel for G > 8 is a variant of its own (two
+    resident workgroups per CU instead of three, deeper prefetch), with its
+    own cost model."""
+    if prob.kernel == _lib.PKV_KERNEL_VALU or (prob.kernel == _lib.PKV_KERNEL_AUTO
+                                               and prob.head_dim != 128):
+        return "valu"
+    return "mfma" if prob.num_q_heads // prob.num_kv_heads <= 8 else "mfma_g16"
+
+
 def load_cost_model(path: str = COST_MODEL_PATH):
-    """(candidates [(path_id, splits)], weights [4][PKV_COST_FEATURES], num_cus)."""
+    """(candidates [(path_id, splits)], {split kernel: weights [4][PKV_COST_FEATURES]},
+    num_cus).  The model has one weight matrix per split kernel."""
     with open(path) as f:
         doc = json.load(f)
     cands = [(PATH_IDS[c["path"]], c["splits"]) for c in doc["candidates"]]
-    weights = np.zeros((4, _lib.PKV_COST_FEATURES), dtype=np.float32)
-    for name, row in doc["weights"].items():
-        weights[PATH_IDS[name]] = np.asarray(row, dtype=np.float32)
+    weights = {}
+    for kernel, rows in doc["weights"].items():
+        w = np.zeros((4, _lib.PKV_COST_FEATURES), dtype=np.float32)
+        for name, row in rows.items():
+            w[PATH_IDS[name]] = np.asarray(row, dtype=np.float32)
+        weights[kernel] = w
     return cands, weights, int(doc["num_cus"])
 
 
 def choose_model(model, prob: _lib.pkv_problem, seq_lens_host):
     """Path name, split cap and predicted µs from the learned cost model
-    (C-ABI pkv_policy_model)."""
+    (C-ABI pkv_policy_model, with the weights of the problem's split kernel)."""
     cands, weights, num_cus = model
-    path, splits, pred = _lib.pkv_policy_model(prob, cands, weights, num_cus, seq_lens_host)
+    path, splits, pred = _lib.pkv_policy_model(prob, cands, weights[split_kernel_of(prob)],
+                                               num_cus, seq_lens_host)
     return PATH_NAMES[path], splits, pred
 
 

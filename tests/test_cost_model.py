@@ -21,11 +21,13 @@ def test_model_file_is_well_formed():
     assert doc["num_cus"] == 256
     cands, weights, cus = engine.load_cost_model()
     assert len(cands) >= 4 and all(p in _lib.PATH_NAMES and s >= 1 for p, s in cands)
-    assert weights.shape == (4, _lib.PKV_COST_FEATURES) and np.isfinite(weights).all()
-    assert abs(weights).max() < 1e3  # the ridge term keeps weights moderate
-    fit = doc["fit"]
-    assert fit["rms_relative_error"] < 0.2
-    assert fit["5fold"]["over_best"] < 0.05
+    assert set(weights) == {"mfma", "mfma_g16", "valu"}  # one per split-kernel variant
+    for w in weights.values():
+        assert w.shape == (4, _lib.PKV_COST_FEATURES) and np.isfinite(w).all()
+        assert abs(w).max() < 1e3  # the ridge term keeps weights moderate
+    for kernel, fit in doc["fit"].items():
+        assert fit["rms_relative_error"] < 0.2, kernel
+        assert fit["5fold"]["over_best"] < 0.05, kernel
 
 
 @pytest.mark.parametrize("name", ["tiny", "long", "bimodal", "zipf", "uniform", "policy_b1",
@@ -38,7 +40,8 @@ def test_c_choice_equals_oracle_on_workloads(name):
                              spec.page_size, 1 << 20, 32768 // spec.page_size, spec.dtype)
     path, s, pred = engine.choose_model((cands, weights, cus), prob, lens)
     named = [(_lib.PATH_NAMES[p], ss) for p, ss in cands]
-    ref = oracle.cost.choose(weights.astype(np.float64), named, lens, spec.num_kv_heads,
+    w = weights[engine.split_kernel_of(prob)]
+    ref = oracle.cost.choose(w.astype(np.float64), named, lens, spec.num_kv_heads,
                              spec.num_q_heads, spec.head_dim, spec.page_size, cus)
     assert (path, s) == ref[:2]
     assert pred == pytest.approx(ref[2], rel=1e-5)
@@ -59,3 +62,20 @@ def test_recorded_heldout_check():
     totals = h["total_us"]
     singles = [v for k, v in totals.items() if ":" in k]
     assert totals["model"] <= min(singles)
+
+
+def test_recorded_shape_checks():
+    """Held-out timings of every candidate at four head shapes (cost_heldout_*.json,
+    never used for fitting): the model's choices stay within 3 % of the best
+    candidate at every shape, and in total are no slower than the table's."""
+    doc = _doc()
+    checks = doc.get("shape_checks", {})
+    if not checks:
+        pytest.skip("shape checks not recorded yet")
+    assert len(checks) >= 4
+    for name, r in checks.items():
+        assert r["seed"] == traces.HELD_OUT_SEED, name
+        assert r["model_over_best"] <= 0.03, name
+    assert (sum(r["total_us"]["model"] for r in checks.values())
+            <= sum(r["total_us"]["table"] for r in checks.values()))
+
