@@ -1,7 +1,7 @@
 """Decode-attention benchmark: µs per decode step and achieved HBM GB/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
-                    [--path bucketed|workqueue|nosplit|padded|policy|model|device] [--kernel auto|valu|mfma]
+                    [--path bucketed|workqueue|nosplit|padded|policy|model|device|selfplan] [--kernel auto|valu|mfma]
 
 One step is the engine's device work for one decode step of one layer: the
 split kernel launch(es) and the merge launch(es) (or the single no-split
@@ -39,7 +39,8 @@ TRAFFIC_PROFILES = {"long": "profiles/split_mfma_long_b1_n32768_traffic.txt",
                     "zipf": "profiles/split_mfma_zipf_b8_traffic.txt",
                     "uniform": "profiles/split_mfma_uniform_b8_traffic.txt",
                     "policy_b64": "profiles/split_mfma_policy_b64_traffic.txt"}
-KERNEL_SOURCES = ("split_mfma.hip", "split_common.h", "device_common.h", "pkv_internal.h")
+KERNEL_SOURCES = ("split_mfma.hip", "split_common.h", "device_common.h", "pkv_internal.h",
+                  "lens_plan.h")
 DEFAULT_PATH = {"tiny": "workqueue", "long": "bucketed", "bimodal": "workqueue",
                 "zipf": "workqueue", "uniform": "workqueue"}
 
@@ -179,9 +180,9 @@ def run_all(args) -> int:
                           "GB/s": round(pr["GB/s"], 1),
                           "pct_of_peak": round(100 * pr["GB/s"] / HBM_PEAK_GBS, 1)}), flush=True)
         if spec.head_dim == 128:
-            for graph in (False, True):
+            for selfplan, graph in ((False, False), (False, True), (True, False), (True, True)):
                 r = timing.time_device_path(w, views, spec.splits, args.steps, args.warmup,
-                                            sync_reps=5, graph=graph)
+                                            sync_reps=5, graph=graph, selfplan=selfplan)
                 kv = int(lens.astype(np.int64).sum()) * spec.num_kv_heads * spec.head_dim * 4
                 gbs = kv / (r["step_us"] * 1e-6) / 1e9
                 print(json.dumps({
@@ -189,7 +190,8 @@ def run_all(args) -> int:
                     "path": r["path"], "splits": spec.splits, "policy_choice": False,
                     "us_per_step": round(r["step_us"], 2), "GB/s": round(gbs, 1),
                     "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-                    "split_us_per_launch": None, "launches_per_step": 3, "kv_bytes": kv,
+                    "split_us_per_launch": None, "launches_per_step": 2 if selfplan else 3,
+                    "kv_bytes": kv,
                     "merge_state_bytes": None,
                     "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1),
                     "cpu_oracle": None}), flush=True)
@@ -216,14 +218,16 @@ def run_all(args) -> int:
     return 0
 
 
-def run_device(args, spec, seed, splits, w, wd, lens) -> int:
+def run_device(args, spec, seed, splits, w, wd, lens, selfplan=False) -> int:
     """The device-planned workqueue step (pkv_plan_device -> pkv_decode_device ->
-    pkv_merge_device, no host work): one JSON line of the same metric, without
-    the per-kernel roofline (the three launches are timed together)."""
+    pkv_merge_device), or the self-planned one (pkv_decode_selfplan ->
+    pkv_merge_selfplan), no host work: one JSON line of the same metric,
+    without the per-kernel roofline (the launches are timed together)."""
     from paged_kv_gqa_block_amd import timing
 
     views = timing.pool_copies(wd, args.copies_gib)
-    r = timing.time_device_path(w, views, splits, args.steps, args.warmup, repeats=1)
+    r = timing.time_device_path(w, views, splits, args.steps, args.warmup, repeats=1,
+                                selfplan=selfplan)
     kv = int(lens.astype("int64").sum()) * spec.num_kv_heads * spec.head_dim * 2 * 2
     gbs = kv / (r["step_us"] * 1e-6) / 1e9
     print(json.dumps({
@@ -231,9 +235,11 @@ def run_device(args, spec, seed, splits, w, wd, lens) -> int:
         "steps": args.steps, "warmup": args.warmup, "us_per_step": round(r["step_us"], 2),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "higher_is_better": True,
         "dtype": spec.dtype, "data": "synthetic",
-        "config": {"workload": describe(spec, "device-planned workqueue", splits, lens),
-                   "seed": seed, "path": "device", "splits": splits, "n_tasks": r["n_tasks"],
-                   "launches_per_step": 3, "kv_bytes": kv,
+        "config": {"workload": describe(spec, ("self-planned" if selfplan else
+                                               "device-planned") + " workqueue", splits, lens),
+                   "seed": seed, "path": "selfplan" if selfplan else "device", "splits": splits,
+                   "n_tasks": r["n_tasks"], "launches_per_step": 2 if selfplan else 3,
+                   "kv_bytes": kv,
                    "sync_wall_us": round(r["sync_wall_us_median"], 1)}}), flush=True)
     return 0
 
@@ -266,8 +272,8 @@ def main(argv=None):
                                               engine.problem_from_workload(w), lens)
     wd = engine.to_device(w)
     engine.validate_inputs(wd)
-    if path == "device":
-        return run_device(args, spec, seed, splits, w, wd, lens)
+    if path in ("device", "selfplan"):
+        return run_device(args, spec, seed, splits, w, wd, lens, selfplan=path == "selfplan")
 
     kernel_used = args.kernel
     if kernel_used == "auto":  # the library's AUTO rule: matrix cores for d = 128

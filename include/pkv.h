@@ -335,6 +335,39 @@ pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan_dev, const
                             hipStream_t stream);
 
 /*
+ * Self-planned workqueue step: the device-planned step without a plan (two
+ * launches, no planner kernel, no plan buffer).  Same method ("Row-local
+ * bounds", "Compact workqueue") and the same tasks, slots and results as
+ * pkv_plan_device + pkv_decode_device + pkv_merge_device: every workgroup of
+ * the split kernel derives the workqueue of the device lengths in its own
+ * LDS (O(B) work per workgroup), and every merge workgroup derives its row's
+ * split count and first slot the same way.
+ *   seq_lens_dev: int32 [B] on the device, read by both calls; a length
+ *     outside [0, max_pages_per_row * P] is treated as an empty row (out 0,
+ *     lse -inf).  It must not change between the two calls.
+ *   work_counter_dev: one int32 of device memory, owned by the caller, zero
+ *     before the first pkv_decode_selfplan (for instance hipMemset once at
+ *     allocation).  The split kernel claims tasks through it and
+ *     pkv_merge_selfplan sets it back to zero, so every pkv_decode_selfplan
+ *     must be followed by its pkv_merge_selfplan before the counter is used
+ *     again; calls that overlap on one counter race.
+ *   st_m, st_l, st_o: as pkv_decode_device (B * Hkv * max_splits slots).
+ * batch <= 1024 and B * Hkv * max_splits <= 2^31 - 1 (else PKV_ERANGE);
+ * matrix-core kernel only: head_dim 128, kernel AUTO or MFMA (else
+ * PKV_ESHAPE).  Errors: PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE,
+ * PKV_EHIP.
+ */
+pkv_status pkv_decode_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                               int32_t max_splits, int32_t* work_counter_dev, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, float* st_m, float* st_l, float* st_o,
+                               hipStream_t stream);
+pkv_status pkv_merge_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                              int32_t max_splits, int32_t* work_counter_dev, const float* st_m,
+                              const float* st_l, const float* st_o, void* out, float* lse,
+                              hipStream_t stream);
+
+/*
  * KV append: store the step's new key and value of every row in the paged
  * pools before attention (the input side of a decode step; not described on
  * the pages).  k_new, v_new: [B][Hkv][d] in the problem dtype.  positions_dev:

@@ -37,7 +37,8 @@ DTYPE_IDS = {"f16": PKV_F16, "bf16": PKV_BF16}
 KERNEL_IDS = {"auto": PKV_KERNEL_AUTO, "valu": PKV_KERNEL_VALU, "mfma": PKV_KERNEL_MFMA}
 
 EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pkv_merge",
-            "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_append_kv",
+            "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_decode_selfplan",
+            "pkv_merge_selfplan", "pkv_append_kv",
             "pkv_policy", "pkv_cost_features", "pkv_policy_model", "pkv_status_str")
 PKV_COST_FEATURES = 7
 
@@ -117,6 +118,10 @@ def _load() -> ctypes.CDLL:
     lib.pkv_decode_device.restype = i32
     lib.pkv_merge_device.argtypes = [prob_p, vp, vp, vp, vp, vp, vp, vp]
     lib.pkv_merge_device.restype = i32
+    lib.pkv_decode_selfplan.argtypes = [prob_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.pkv_decode_selfplan.restype = i32
+    lib.pkv_merge_selfplan.argtypes = [prob_p, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.pkv_merge_selfplan.restype = i32
     lib.pkv_append_kv.argtypes = [prob_p, vp, vp, vp, vp, vp, vp, vp]
     lib.pkv_append_kv.restype = i32
     lib.pkv_policy.argtypes = [ctypes.POINTER(pkv_policy_table), i32, i32,
@@ -252,6 +257,21 @@ def pkv_merge_device(prob: pkv_problem, plan_dev, st_m, st_l, st_o, out, lse=Non
     _check("pkv_merge_device", LIB.pkv_merge_device(
         ctypes.byref(prob), _ptr(plan_dev), _ptr(st_m), _ptr(st_l), _ptr(st_o), _ptr(out),
         _ptr(lse), _stream(stream)))
+
+
+def pkv_decode_selfplan(prob: pkv_problem, seq_lens_dev, max_splits: int, work_counter_dev, q,
+                        k_pool, v_pool, block_table, st_m, st_l, st_o, stream=None) -> None:
+    _check("pkv_decode_selfplan", LIB.pkv_decode_selfplan(
+        ctypes.byref(prob), _ptr(seq_lens_dev), max_splits, _ptr(work_counter_dev), _ptr(q),
+        _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(st_m), _ptr(st_l), _ptr(st_o),
+        _stream(stream)))
+
+
+def pkv_merge_selfplan(prob: pkv_problem, seq_lens_dev, max_splits: int, work_counter_dev, st_m,
+                       st_l, st_o, out, lse=None, stream=None) -> None:
+    _check("pkv_merge_selfplan", LIB.pkv_merge_selfplan(
+        ctypes.byref(prob), _ptr(seq_lens_dev), max_splits, _ptr(work_counter_dev), _ptr(st_m),
+        _ptr(st_l), _ptr(st_o), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def pkv_append_kv(prob: pkv_problem, k_new, v_new, block_table, positions_dev, k_pool, v_pool,

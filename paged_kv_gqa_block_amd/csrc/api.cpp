@@ -262,6 +262,88 @@ extern "C" pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan
   return launch_merge(*prob, a, stream);
 }
 
+// ---- self-planned workqueue step --------------------------------------------
+
+namespace {
+
+// Shared checks of the self-planned entry points.
+pkv_status check_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                          int32_t max_splits, const int32_t* work_counter_dev) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  if (!seq_lens_dev || !work_counter_dev) return PKV_EINVAL;
+  if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
+  if (prob->batch > kMaxLensRows) return PKV_ERANGE;
+  // Task indices and slots are 32-bit: bound the largest task count.
+  if (int64_t(prob->batch) * prob->num_kv_heads * max_splits > INT32_MAX) return PKV_ERANGE;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_decode_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                                          int32_t max_splits, int32_t* work_counter_dev,
+                                          const void* q, const void* k_pool, const void* v_pool,
+                                          const int32_t* block_table, float* st_m, float* st_l,
+                                          float* st_o, hipStream_t stream) {
+  pkv_status st = check_selfplan(prob, seq_lens_dev, max_splits, work_counter_dev);
+  if (st != PKV_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !st_m || !st_l || !st_o) return PKV_EINVAL;
+  if (prob->head_dim != 128 || prob->kernel == PKV_KERNEL_VALU) return PKV_ESHAPE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return PKV_EHIP;
+  SplitArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens_dev;
+  a.st_m = st_m;
+  a.st_l = st_l;
+  a.st_o = st_o;
+  a.num_q_heads = prob->num_q_heads;
+  a.num_kv_heads = prob->num_kv_heads;
+  a.max_pages = prob->max_pages_per_row;
+  a.splits = max_splits;
+  a.scale_log2 = prob->sm_scale * kLog2e;
+  a.bucket_row0 = -1;
+  a.num_rows = prob->batch;
+  a.work_counter = work_counter_dev;
+  // The persistent grid of pkv_decode_device.
+  const int per_cu = (prob->num_q_heads / prob->num_kv_heads <= 8) ? 3 : 2;
+  const int64_t upper = int64_t(prob->batch) * prob->num_kv_heads * max_splits;
+  const int grid = static_cast<int>(std::min<int64_t>(upper, int64_t(per_cu) * cus));
+  a.num_items = grid;
+  return launch_split(*prob, kModeLens, prob->kernel, a, grid, stream);
+}
+
+extern "C" pkv_status pkv_merge_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                                         int32_t max_splits, int32_t* work_counter_dev,
+                                         const float* st_m, const float* st_l, const float* st_o,
+                                         void* out, float* lse, hipStream_t stream) {
+  pkv_status st = check_selfplan(prob, seq_lens_dev, max_splits, work_counter_dev);
+  if (st != PKV_OK) return st;
+  if (!st_m || !st_l || !st_o || !out) return PKV_EINVAL;
+  MergeArgs a{};
+  a.st_m = st_m;
+  a.st_l = st_l;
+  a.st_o = st_o;
+  a.out = out;
+  a.lse = lse;
+  a.num_q_heads = prob->num_q_heads;
+  a.num_kv_heads = prob->num_kv_heads;
+  a.splits = max_splits;
+  a.num_rows = prob->batch;
+  a.mode = kModeLens;
+  a.bucket_row0 = -1;
+  a.seq_lens = seq_lens_dev;
+  a.max_pages = prob->max_pages_per_row;
+  a.work_counter = work_counter_dev;  // the merge resets the split kernel's counter
+  return launch_merge(*prob, a, stream);
+}
+
 extern "C" pkv_status pkv_append_kv(const pkv_problem* prob, const void* k_new,
                                     const void* v_new, const int32_t* block_table,
                                     const int32_t* positions_dev, void* k_pool, void* v_pool,

@@ -97,6 +97,33 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
       __builtin_amdgcn_ds_bpermute(((lane ^ mask) & 63) << 2, __float_as_int(x)));
 }
 
+// Integer maximum over the wave; every lane gets it.
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1)
+    x = max(x, __builtin_amdgcn_ds_bpermute(((__lane_id() ^ sh) & 63) << 2, x));
+  return x;
+}
+
+// Integer sum over the wave; every lane gets it.
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1)
+    x += __builtin_amdgcn_ds_bpermute(((__lane_id() ^ sh) & 63) << 2, x);
+  return x;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan_i(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute(((lane - sh) & 63) << 2, x);
+    if (lane >= sh) x += y;
+  }
+  return x;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }

@@ -1,0 +1,138 @@
+// Self-planned workqueue: the compact workqueue of the device lengths,
+// derived inside the split and merge kernels instead of by a planner launch.
+//
+// Method: PersistentKV summary pages, "Methodology / 1. Native block-table
+// decode engine", "Row-local bounds" and "Compact workqueue".  The split rule
+// is the workqueue planners' (host and device): pps = max(1, ceil(T_max / S))
+// pages shared by the batch, ceil(T_i / pps) splits for row i, tasks in
+// (row, kv_head, split) order, so task t and its state slot t are exactly
+// those of the planned workqueue.  Rows whose length lies outside
+// [0, max_pages * 16] are treated as empty.
+#pragma once
+
+#include "device_common.h"
+#include "pkv_internal.h"
+#include "split_common.h"
+
+namespace pkv {
+
+__device__ __forceinline__ int lens_valid(int n, int64_t cap) { return (n < 0 || n > cap) ? 0 : n; }
+
+// Every workgroup of the split kernel builds the row offsets of the task list
+// in LDS: s_len[r] = N_r (invalid lengths as 0), s_off[r] = first task of row
+// r, s_off[B] = task count.  NT threads, each owning up to kMaxLensRows / NT
+// consecutive rows; s_red holds one int per wave.  Returns pps.  Ends with a
+// barrier.
+template <int NT>
+__device__ __forceinline__ int lens_plan_in_lds(const int32_t* __restrict__ seq_lens, int b,
+                                                int hkv, int splits, int64_t cap, int* s_len,
+                                                int* s_off, int* s_red) {
+  constexpr int kPer = kMaxLensRows / NT;
+  constexpr int kWaves = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = tid * kPer;
+  int n[kPer];
+  int t_max = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    n[i] = (r0 + i < b) ? lens_valid(seq_lens[r0 + i], cap) : 0;
+    t_max = max(t_max, (n[i] + 15) >> 4);
+  }
+  t_max = wave_max_i(t_max);
+  if (lane == 0) s_red[wave] = t_max;
+  __syncthreads();
+  t_max = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t_max = max(t_max, s_red[w]);
+  const int pps = max(1, (t_max + splits - 1) / splits);
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) local += hkv * ((((n[i] + 15) >> 4) + pps - 1) / pps);
+  const int incl = wave_scan_i(local);
+  __syncthreads();  // every wave has read s_red
+  if (lane == 63) s_red[wave] = incl;
+  __syncthreads();
+  int off = incl - local, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    off += (w < wave) ? s_red[w] : 0;
+    total += s_red[w];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (r0 + i < b) {
+      s_len[r0 + i] = n[i];
+      s_off[r0 + i] = off;
+      off += hkv * ((((n[i] + 15) >> 4) + pps - 1) / pps);
+    }
+  }
+  if (tid == 0) s_off[b] = total;
+  __syncthreads();
+  return pps;
+}
+
+// Task t (< s_off[B]) of the self-planned workqueue; its state slot is t.
+// t is workgroup-uniform, so every value read from LDS, and every quotient,
+// is too: each is moved to a scalar register (the task then costs no vector
+// registers, as a task record loaded from memory does not).
+__device__ __forceinline__ Task lens_task(int t, const int* s_len, const int* s_off, int b,
+                                          int hkv, int pps) {
+  int lo = 0, hi = b;  // s_off[lo] <= t < s_off[hi]; rows without tasks are skipped
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (__builtin_amdgcn_readfirstlane(s_off[mid]) <= t) lo = mid;
+    else hi = mid;
+  }
+  Task tk;
+  tk.row = lo;
+  const int n = __builtin_amdgcn_readfirstlane(s_len[lo]);
+  const int off0 = __builtin_amdgcn_readfirstlane(s_off[lo]);
+  const int off1 = __builtin_amdgcn_readfirstlane(s_off[lo + 1]);
+  const int pages = (n + 15) >> 4;
+  const int ns = __builtin_amdgcn_readfirstlane((off1 - off0) / hkv);
+  const int k = t - off0;
+  tk.g = __builtin_amdgcn_readfirstlane(k / ns);
+  const int s = k - tk.g * ns;
+  tk.page_begin = s * pps;
+  const int pe = min(tk.page_begin + pps, pages);
+  tk.tok_end = min(pe * 16, n);
+  tk.slot = t;
+  tk.empty = false;
+  return tk;
+}
+
+// Merge side: the split count of `row` and its first state slot
+// (Hkv * sum of the earlier rows' split counts), from the device lengths.
+// NT threads stride over the rows; s_red holds one int per wave.  Every
+// thread gets the result.
+template <int NT>
+__device__ __forceinline__ void lens_row_slots(const int32_t* __restrict__ seq_lens, int b,
+                                               int hkv, int splits, int64_t cap, int row,
+                                               int* s_red, int* nsplit_out,
+                                               int64_t* first_slot_out) {
+  constexpr int kWaves = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int t_max = 0;
+  for (int r = tid; r < b; r += NT) t_max = max(t_max, (lens_valid(seq_lens[r], cap) + 15) >> 4);
+  t_max = wave_max_i(t_max);
+  if (lane == 0) s_red[wave] = t_max;
+  __syncthreads();
+  t_max = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t_max = max(t_max, s_red[w]);
+  const int pps = max(1, (t_max + splits - 1) / splits);
+  int before = 0;
+  for (int r = tid; r < row; r += NT)
+    before += (((lens_valid(seq_lens[r], cap) + 15) >> 4) + pps - 1) / pps;
+  before = wave_sum_i(before);
+  __syncthreads();  // every wave has read s_red
+  if (lane == 0) s_red[wave] = before;
+  __syncthreads();
+  int64_t sum = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) sum += s_red[w];
+  *nsplit_out = (((lens_valid(seq_lens[row], cap) + 15) >> 4) + pps - 1) / pps;
+  *first_slot_out = sum * hkv;
+}
+
+}  // namespace pkv

@@ -15,6 +15,7 @@
 // 4 outputs); split groups are then combined through LDS.
 #include "device_common.h"
 #include "launch_limits.h"
+#include "lens_plan.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -37,7 +38,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int hh = h - g * G;
   int row, nsplit;
   int64_t base;  // first state slot of this (row, kv head)
-  if (a.mode == kModeWorkqueue && a.uniform_nsplit > 0) {
+  __shared__ int s_red[4];
+  if (a.mode == kModeLens) {
+    // Self-planned workqueue: the row's split count and first slot follow
+    // from the device lengths (the split kernel derived the same tasks).
+    row = ri;
+    int64_t first;
+    lens_row_slots<256>(a.seq_lens, a.num_rows, hkv, a.splits, int64_t(a.max_pages) * 16, row,
+                        s_red, &nsplit, &first);
+    base = first + int64_t(g) * nsplit;
+  } else if (a.mode == kModeWorkqueue && a.uniform_nsplit > 0) {
     // Every row has the same split count, so the row's first slot follows
     // from its index and the plan's row arrays need not be read (one
     // dependent memory round trip less).
@@ -59,6 +69,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   // The split kernel has finished (stream order): reset the persistent
   // kernel's work counter for the next step on this plan.
   if (a.device_plan && item == 0 && t == 0) a.device_plan[a.device_plan[kTotalWords]] = 0;
+  if (a.work_counter && item == 0 && t == 0) *a.work_counter = 0;
 
   float mloc = kNegInf, lloc = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -157,11 +168,12 @@ pkv_status launch_split_mfma(const pkv_problem& p, int mode, const SplitArgs& a,
 // wherever it applies (d = 128, any G <= 16) -- on MI355X it is faster than the
 // vector-ALU kernel on every measured workload -- and the vector-ALU kernel for
 // d = 64 (G <= 8).
-// The persistent (device-planned) mode exists only in the matrix-core kernel.
+// The persistent modes (device-planned and self-planned) exist only in the
+// matrix-core kernel.
 pkv_status launch_split(const pkv_problem& p, int mode, int kernel, const SplitArgs& a, int grid,
                         hipStream_t s) {
   if (grid <= 0) return PKV_OK;
-  if (mode == kModePersistent)
+  if (mode == kModePersistent || mode == kModeLens)
     return kernel == PKV_KERNEL_VALU ? PKV_ESHAPE : launch_split_mfma(p, mode, a, grid, s);
   if (kernel == PKV_KERNEL_MFMA || (kernel == PKV_KERNEL_AUTO && p.head_dim == 128))
     return launch_split_mfma(p, mode, a, grid, s);

@@ -91,7 +91,14 @@ PlanCounts count_plan(const pkv_problem& p, const int32_t* lens, int32_t path, i
                       const int32_t* order);
 
 // Which grid a split-kernel launch walks.
-enum SplitMode : int { kModeWorkqueue = 0, kModeBucket = 1, kModeNoSplit = 2, kModePersistent = 3 };
+enum SplitMode : int {
+  kModeWorkqueue = 0,
+  kModeBucket = 1,
+  kModeNoSplit = 2,
+  kModePersistent = 3,  // persistent grid over a device-built plan
+  kModeLens = 4,        // persistent grid, tasks derived from the lengths in-kernel
+};
+constexpr int kMaxLensRows = 1024;  // batch limit of the self-planned step
 
 // Everything a split / no-split kernel needs; passed by value as a kernel
 // argument.  Pointers are device pointers.
@@ -123,6 +130,8 @@ struct SplitArgs {
   int32_t bucket_row0;  // bucket: its only row when it has one, else -1
   int32_t num_items;    // grid items (tasks, bucket slots or rows * Hkv)
   float scale_log2;   // sm_scale * log2(e)
+  int32_t num_rows;        // lens mode: B
+  int32_t* work_counter;   // lens mode: task claim counter (zero between steps)
 };
 
 struct MergeArgs {
@@ -142,6 +151,9 @@ struct MergeArgs {
   int32_t bucket_row0;  // bucket: its only row when it has one, else -1
   int32_t* device_plan;  // device-planned step: the merge resets its work counter; else null
   int32_t uniform_nsplit;  // workqueue: the split count every row shares (> 0), else 0
+  const int32_t* seq_lens;  // lens mode: device lengths (slots derived in-kernel)
+  int32_t max_pages;        // lens mode: block-table row stride (length bound)
+  int32_t* work_counter;    // lens mode: the split kernel's claim counter, reset here
 };
 
 struct AppendArgs {

@@ -25,24 +25,6 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
-__device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1)
-    x = max(x, __builtin_amdgcn_ds_bpermute(((__lane_id() ^ sh) & 63) << 2, x));
-  return x;
-}
-
-// Inclusive prefix sum over the wave.
-__device__ __forceinline__ int wave_scan_i(int x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int sh = 1; sh < 64; sh <<= 1) {
-    const int y = __builtin_amdgcn_ds_bpermute(((lane - sh) & 63) << 2, x);
-    if (lane >= sh) x += y;
-  }
-  return x;
-}
-
 __device__ __forceinline__ int valid_len(int n, int64_t cap) { return (n < 0 || n > cap) ? -1 : n; }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_workqueue_kernel(
@@ -152,9 +134,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_workqueue_kernel(
     plan[off_tasks + kTaskWords * n_tasks] = 0;  // work counter of the persistent kernel
   }
   // Bad-row count: per-wave sums, one atomic-free combine.
-  int b = bad;
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) b += __builtin_amdgcn_ds_bpermute(((lane ^ sh) & 63) << 2, b);
+  const int b = wave_sum_i(bad);
   __syncthreads();
   if (lane == 0) s_wave[wave] = b;
   __syncthreads();

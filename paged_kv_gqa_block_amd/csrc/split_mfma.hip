@@ -31,6 +31,7 @@
 // Method: PersistentKV summary pages, "Methodology / 1. Native block-table
 // decode engine" (GQA over paged KV read through the block table, partial
 // online-softmax state per disjoint split, empty splits write neutral state).
+#include "lens_plan.h"
 #include "split_common.h"
 
 namespace pkv {
@@ -316,7 +317,9 @@ __device__ __forceinline__ void mfma_task(const SplitArgs& a, Task tk, MfmaShare
 
 // Grid modes: one workgroup per workqueue task / bucket slot / (row, KV head);
 // or persistent: a fixed grid claiming tasks of a device-built workqueue whose
-// task count is read from the plan on the device.
+// task count is read from the plan on the device; or self-planned: the same
+// persistent grid over the workqueue each workgroup derives from the device
+// lengths in LDS (no plan in memory).
 // With one page in flight per wave (PF = 1) the kernel fits in 168 registers
 // per lane without spilling, so three waves share each SIMD (three
 // workgroups per CU) instead of the two the compiler would otherwise pick.
@@ -344,6 +347,28 @@ void split_mfma_kernel(SplitArgs a) {
       __syncthreads();
       t = s_task;
     }
+  } else if constexpr (MODE == kModeLens) {
+    // Same claim protocol as the persistent mode; the task list is the
+    // workqueue of the device lengths, rebuilt in LDS by every workgroup
+    // (O(B) work, B <= kMaxLensRows), and the counter is the caller's.
+    __shared__ int s_len[kMaxLensRows];
+    __shared__ int s_off[kMaxLensRows + 1];
+    __shared__ int s_red[NW];
+    __shared__ int s_task;
+    const int b = a.num_rows, hkv = a.num_kv_heads;
+    const int pps = __builtin_amdgcn_readfirstlane(lens_plan_in_lds<NW * 64>(
+        a.seq_lens, b, hkv, a.splits, int64_t(a.max_pages) * 16, s_len, s_off, s_red));
+    const int n_tasks = __builtin_amdgcn_readfirstlane(s_off[b]);
+    const int grid = static_cast<int>(gridDim.x);
+    int t = static_cast<int>(blockIdx.x);
+    while (t < n_tasks) {
+      mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, lens_task(t, s_len, s_off, b, hkv, pps), sh);
+      if (n_tasks <= grid) break;
+      __syncthreads();
+      if (threadIdx.x == 0) s_task = grid + atomicAdd(a.work_counter, 1);
+      __syncthreads();
+      t = __builtin_amdgcn_readfirstlane(s_task);
+    }
   } else {
     const Task tk = decode_task<MODE>(a, blockIdx.x);
     if constexpr (MODE == kModeBucket) {
@@ -368,9 +393,12 @@ pkv_status launch_mfma_modes(int mode, const SplitArgs& a, int grid, hipStream_t
   else if (mode == kModeNoSplit)
     hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeNoSplit>), dim3(grid), block, 0,
                        s, a);
-  else
+  else if (mode == kModePersistent)
     hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModePersistent>), dim3(grid), block,
                        0, s, a);
+  else
+    hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeLens>), dim3(grid), block, 0, s,
+                       a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

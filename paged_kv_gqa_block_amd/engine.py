@@ -125,6 +125,29 @@ class DeviceStep:
         return self.out, self.lse
 
 
+class SelfPlannedStep(DeviceStep):
+    """Self-planned workqueue step: the device-planned step in two launches.
+
+    ``run`` enqueues pkv_decode_selfplan -> pkv_merge_selfplan: the split and
+    merge kernels derive the workqueue of the device lengths themselves, so
+    there is no planner launch and no plan buffer, only a one-word claim
+    counter (zeroed here once; the merge leaves it zeroed).
+    """
+
+    def __init__(self, prob: _lib.pkv_problem, splits: int, device="cuda"):
+        super().__init__(prob, splits, device)
+        del self.plan_dev, self.bad_rows
+        self.counter = torch.zeros(1, dtype=torch.int32, device=self.device)
+
+    def run(self, w: dict, stream=None):
+        _lib.pkv_decode_selfplan(self.prob, w["seq_lens"], self.splits, self.counter, w["q"],
+                                 w["k_pool"], w["v_pool"], w["block_table"], self.st_m,
+                                 self.st_l, self.st_o, stream=stream)
+        _lib.pkv_merge_selfplan(self.prob, w["seq_lens"], self.splits, self.counter, self.st_m,
+                                self.st_l, self.st_o, self.out, self.lse, stream=stream)
+        return self.out, self.lse
+
+
 def load_policy_table(path: str = POLICY_TABLE_PATH):
     """Rules [(b_lo, b_hi, nmax_lo, nmax_hi, path_id, splits)] from the JSON table."""
     with open(path) as f:

@@ -13,6 +13,7 @@ import math
 import statistics
 import time
 
+import numpy as np
 import torch
 
 from . import engine
@@ -181,13 +182,15 @@ def time_read_probe(w: dict, views, path: str, splits: int, steps: int = 50,
 
 
 def time_device_path(w: dict, views, splits: int, steps: int = 50, warmup: int = 10,
-                     sync_reps: int = 20, repeats: int = 5, graph: bool = False) -> dict:
+                     sync_reps: int = 20, repeats: int = 5, graph: bool = False,
+                     selfplan: bool = False) -> dict:
     """Times the device-planned workqueue step (plan + persistent split + merge
-    on the GPU, no host work).  With ``graph``, each pool copy's step is
-    captured once in a HIP graph and replayed."""
-    wd = views[0]
+    on the GPU, no host work), or with ``selfplan`` the self-planned step
+    (persistent split + merge deriving the workqueue in-kernel).  With
+    ``graph``, each pool copy's step is captured once in a HIP graph and
+    replayed."""
     prob = engine.problem_from_workload(w, "auto")
-    step = engine.DeviceStep(prob, splits)
+    step = (engine.SelfPlannedStep if selfplan else engine.DeviceStep)(prob, splits)
     n = len(views)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -228,11 +231,14 @@ def time_device_path(w: dict, views, splits: int, steps: int = 50, warmup: int =
             one(i)
             torch.cuda.synchronize()
             sync_us.append((time.perf_counter() - t) * 1e6)
-    plan = step.plan_dev.cpu().numpy()
+    pages = (w["seq_lens"].numpy().astype(np.int64) + 15) // 16
+    pps = max(1, -(-int(pages.max(initial=0)) // splits))
+    n_tasks = int(prob.num_kv_heads * (-(-pages // pps)).sum())
     return {
-        "path": "workqueue_device" + ("_graph" if graph else ""),
+        "path": ("workqueue_selfplan" if selfplan else "workqueue_device") +
+                ("_graph" if graph else ""),
         "splits": splits,
-        "n_tasks": int(plan[6]),
+        "n_tasks": n_tasks,
         "step_us": statistics.median(runs),
         "step_us_runs": [round(x, 2) for x in runs],
         "sync_wall_us_median": statistics.median(sync_us) if sync_us else None,

@@ -294,6 +294,41 @@ def test_device_plan_entry_points_validate_before_launch():
     assert e.value.status == PKV_EINVAL
 
 
+def test_selfplan_entry_points_validate_before_launch():
+    prob = _prob(2)
+    fake = 0x1000  # never dereferenced: every call below fails validation first
+    args = (fake, fake, fake, fake, fake, fake, fake)  # q, k, v, table, st_m, st_l, st_o
+    with pytest.raises(PkvError) as e:  # no claim counter
+        _lib.pkv_decode_selfplan(prob, fake, 8, None, *args)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_decode_selfplan(prob, fake, 0, fake, *args)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:  # one row past the in-kernel planning limit
+        _lib.pkv_decode_selfplan(_prob(1025), fake, 8, fake, *args)
+    assert e.value.status == PKV_ERANGE
+    with pytest.raises(PkvError) as e:  # B * Hkv * S past 32-bit task indices
+        _lib.pkv_decode_selfplan(_prob(1024, hq=4096, hkv=4096), fake, 65535, fake, *args)
+    assert e.value.status == PKV_ERANGE
+    with pytest.raises(PkvError) as e:  # d = 64 has no persistent kernel
+        _lib.pkv_decode_selfplan(_prob(2, d=64), fake, 8, fake, *args)
+    assert e.value.status == PKV_ESHAPE
+    valu = _prob(2)
+    valu.kernel = _lib.PKV_KERNEL_VALU
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_decode_selfplan(valu, fake, 8, fake, *args)
+    assert e.value.status == PKV_ESHAPE
+    with pytest.raises(PkvError) as e:  # missing states
+        _lib.pkv_decode_selfplan(prob, fake, 8, fake, fake, fake, fake, fake, None, fake, fake)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:  # missing output
+        _lib.pkv_merge_selfplan(prob, fake, 8, fake, fake, fake, fake, None)
+    assert e.value.status == PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_merge_selfplan(_prob(1025), fake, 8, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ERANGE
+
+
 def test_append_validates_before_launch():
     prob = _prob(2)
     fake = 0x1000
