@@ -308,16 +308,18 @@ pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_model* model
  * [0, max_pages_per_row * P] is planned as an empty row, and the number of
  * such rows is written to *bad_rows_dev when it is not NULL.
  *
- * pkv_decode_device runs the split kernel as a persistent grid (as many
- * workgroups as fit on the device at once, at most B * Hkv * max_splits):
- * workgroup w runs task w, and further tasks are claimed through a work
- * counter kept in plan word [total_words] (just past the task list;
- * pkv_plan_bytes leaves room for it).  pkv_plan_device zeroes the counter and pkv_merge_device resets it, so
- * every pkv_decode_device must follow a pkv_plan_device or a pkv_merge_device
- * on the same plan; calls that overlap on one plan race.  It writes st_m, st_l, st_o exactly as pkv_decode does for the
- * WORKQUEUE path (slot = task index); the state buffers must hold
- * B * Hkv * max_splits slots.  Matrix-core kernel only: head_dim 128, and
- * kernel PKV_KERNEL_AUTO or PKV_KERNEL_MFMA (else PKV_ESHAPE).
+ * pkv_decode_device runs the split kernel as a persistent grid (about as
+ * many workgroups as fit on the device at once, at most B * Hkv *
+ * max_splits): workgroup w runs task w, and further tasks are claimed
+ * through a work counter kept in plan word [total_words] (just past the task
+ * list; pkv_plan_bytes leaves room for it).  pkv_plan_device zeroes the
+ * counter and pkv_merge_device resets it, so every pkv_decode_device must
+ * follow a pkv_plan_device or a pkv_merge_device on the same plan; calls
+ * that overlap on one plan race.  It writes st_m, st_l, st_o exactly as
+ * pkv_decode does for the WORKQUEUE path (slot = task index); the state
+ * buffers must hold B * Hkv * max_splits slots.  The split kernel is chosen
+ * and the shape checked as for pkv_decode (PKV_ESHAPE where no kernel covers
+ * it).
  *
  * pkv_merge_device combines the states into out / lse (lse may be NULL) using
  * the device plan's row arrays.  The three calls are ordered on `stream`.
@@ -353,9 +355,8 @@ pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan_dev, const
  *     again; calls that overlap on one counter race.
  *   st_m, st_l, st_o: as pkv_decode_device (B * Hkv * max_splits slots).
  * batch <= 1024 and B * Hkv * max_splits <= 2^31 - 1 (else PKV_ERANGE);
- * matrix-core kernel only: head_dim 128, kernel AUTO or MFMA (else
- * PKV_ESHAPE).  Errors: PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE,
- * PKV_EHIP.
+ * the split kernel is chosen and the shape checked as for pkv_decode.
+ * Errors: PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE, PKV_EHIP.
  */
 pkv_status pkv_decode_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
                                int32_t max_splits, int32_t* work_counter_dev, const void* q,

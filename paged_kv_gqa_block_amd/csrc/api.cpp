@@ -27,6 +27,17 @@ pkv_status check_plan(const pkv_problem* prob, const void* plan_host, const int3
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Workgroups per CU of a persistent grid: the split kernel's resident count.
+// Matrix cores: three for G <= 8 (held to 168 registers), two for G = 16.
+// Vector ALU: two (one or two resident, by head size and group; a grid
+// larger than the resident set only delays the surplus workgroups' first
+// tasks).
+int persistent_per_cu(const pkv_problem* p) {
+  const bool mfma = p->kernel == PKV_KERNEL_MFMA || (p->kernel == PKV_KERNEL_AUTO && p->head_dim == 128);
+  if (!mfma) return 2;
+  return (p->num_q_heads / p->num_kv_heads <= 8) ? 3 : 2;
+}
+
 // Shapes the chosen split kernel covers: matrix cores d = 128, G <= 16;
 // vector ALU d = 64 or 128, G <= 8; AUTO is matrix cores for d = 128.
 pkv_status check_kernel_shape(const pkv_problem* p) {
@@ -204,7 +215,8 @@ extern "C" pkv_status pkv_decode_device(const pkv_problem* prob, const void* pla
   if (!plan_dev || !q || !k_pool || !v_pool || !block_table || !st_m || !st_l || !st_o)
     return PKV_EINVAL;
   if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
-  if (prob->head_dim != 128 || prob->kernel == PKV_KERNEL_VALU) return PKV_ESHAPE;
+  st = check_kernel_shape(prob);
+  if (st != PKV_OK) return st;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -228,9 +240,9 @@ extern "C" pkv_status pkv_decode_device(const pkv_problem* prob, const void* pla
   // located from the plan header on the device.
   a.device_plan = const_cast<int32_t*>(plan);
   a.bucket_row0 = -1;
-  // As many workgroups as can be resident (three per CU for G <= 8, two for
-  // larger groups), never more than the largest task count.
-  const int per_cu = (prob->num_q_heads / prob->num_kv_heads <= 8) ? 3 : 2;
+  // As many workgroups as can be resident, never more than the largest task
+  // count.
+  const int per_cu = persistent_per_cu(prob);
   const int64_t upper = int64_t(prob->batch) * prob->num_kv_heads * max_splits;
   const int grid = static_cast<int>(std::min<int64_t>(upper, int64_t(per_cu) * cus));
   a.num_items = grid;
@@ -289,7 +301,8 @@ extern "C" pkv_status pkv_decode_selfplan(const pkv_problem* prob, const int32_t
   pkv_status st = check_selfplan(prob, seq_lens_dev, max_splits, work_counter_dev);
   if (st != PKV_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !st_m || !st_l || !st_o) return PKV_EINVAL;
-  if (prob->head_dim != 128 || prob->kernel == PKV_KERNEL_VALU) return PKV_ESHAPE;
+  st = check_kernel_shape(prob);
+  if (st != PKV_OK) return st;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -312,7 +325,7 @@ extern "C" pkv_status pkv_decode_selfplan(const pkv_problem* prob, const int32_t
   a.num_rows = prob->batch;
   a.work_counter = work_counter_dev;
   // The persistent grid of pkv_decode_device.
-  const int per_cu = (prob->num_q_heads / prob->num_kv_heads <= 8) ? 3 : 2;
+  const int per_cu = persistent_per_cu(prob);
   const int64_t upper = int64_t(prob->batch) * prob->num_kv_heads * max_splits;
   const int grid = static_cast<int>(std::min<int64_t>(upper, int64_t(per_cu) * cus));
   a.num_items = grid;

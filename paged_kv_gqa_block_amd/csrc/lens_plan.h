@@ -101,6 +101,31 @@ __device__ __forceinline__ Task lens_task(int t, const int* s_len, const int* s_
   return tk;
 }
 
+// Self-planned persistent grid: the claim protocol of persistent_plan_loop
+// over the workqueue of the device lengths, rebuilt in LDS by every
+// workgroup (O(B) work, B <= kMaxLensRows); the counter is the caller's.
+template <int NT, typename RunTask>
+__device__ __forceinline__ void lens_loop(const SplitArgs& a, RunTask run) {
+  __shared__ int s_len[kMaxLensRows];
+  __shared__ int s_off[kMaxLensRows + 1];
+  __shared__ int s_red[NT / 64];
+  __shared__ int s_task;
+  const int b = a.num_rows, hkv = a.num_kv_heads;
+  const int pps = __builtin_amdgcn_readfirstlane(lens_plan_in_lds<NT>(
+      a.seq_lens, b, hkv, a.splits, int64_t(a.max_pages) * 16, s_len, s_off, s_red));
+  const int n_tasks = __builtin_amdgcn_readfirstlane(s_off[b]);
+  const int grid = static_cast<int>(gridDim.x);
+  int t = static_cast<int>(blockIdx.x);
+  while (t < n_tasks) {
+    run(lens_task(t, s_len, s_off, b, hkv, pps));
+    if (n_tasks <= grid) break;
+    __syncthreads();
+    if (threadIdx.x == 0) s_task = grid + atomicAdd(a.work_counter, 1);
+    __syncthreads();
+    t = __builtin_amdgcn_readfirstlane(s_task);
+  }
+}
+
 // Merge side: the split count of `row` and its first state slot
 // (Hkv * sum of the earlier rows' split counts), from the device lengths.
 // NT threads stride over the rows; s_red holds one int per wave.  Every

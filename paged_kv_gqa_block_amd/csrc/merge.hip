@@ -167,14 +167,10 @@ pkv_status launch_split_mfma(const pkv_problem& p, int mode, const SplitArgs& a,
 // Chooses the split-kernel arithmetic.  AUTO takes the matrix-core kernel
 // wherever it applies (d = 128, any G <= 16) -- on MI355X it is faster than the
 // vector-ALU kernel on every measured workload -- and the vector-ALU kernel for
-// d = 64 (G <= 8).
-// The persistent modes (device-planned and self-planned) exist only in the
-// matrix-core kernel.
+// d = 64 (G <= 8).  Every grid mode exists in both kernels.
 pkv_status launch_split(const pkv_problem& p, int mode, int kernel, const SplitArgs& a, int grid,
                         hipStream_t s) {
   if (grid <= 0) return PKV_OK;
-  if (mode == kModePersistent || mode == kModeLens)
-    return kernel == PKV_KERNEL_VALU ? PKV_ESHAPE : launch_split_mfma(p, mode, a, grid, s);
   if (kernel == PKV_KERNEL_MFMA || (kernel == PKV_KERNEL_AUTO && p.head_dim == 128))
     return launch_split_mfma(p, mode, a, grid, s);
   return launch_split_valu(p, mode, a, grid, s);

@@ -59,6 +59,31 @@ __device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
   return t;
 }
 
+// Persistent grid over a device-built workqueue plan: workgroup w first runs
+// task w; further tasks (grid + k for the k-th claim) come from a
+// device-scope counter, zeroed by the device planner and reset by the device
+// merge, so they go to whichever workgroups are running.  A workgroup exits
+// once its task index passes the task count (or at once after its first task
+// when the grid covers every task), and none ever waits on another.
+// run(Task) processes one task and may reuse LDS: the barrier before each
+// claim orders it against the next task.
+template <typename RunTask>
+__device__ __forceinline__ void persistent_plan_loop(const SplitArgs& a, RunTask run) {
+  __shared__ int s_task;
+  const int n_tasks = a.device_plan[kNumTasks];
+  const int grid = static_cast<int>(gridDim.x);
+  int32_t* counter = a.device_plan + a.device_plan[kTotalWords];
+  int t = static_cast<int>(blockIdx.x);
+  while (t < n_tasks) {
+    run(decode_task<kModeWorkqueue>(a, t));
+    if (n_tasks <= grid) break;
+    __syncthreads();  // LDS (and s_task) are reused by the next task
+    if (threadIdx.x == 0) s_task = grid + atomicAdd(counter, 1);
+    __syncthreads();
+    t = s_task;
+  }
+}
+
 // Neutral state (-inf, 0, 0) of an empty bucket slot.
 template <int NW>
 __device__ __forceinline__ void write_neutral(const SplitArgs& a, const Task& t, int G, int D) {

@@ -328,47 +328,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PF == 1
 void split_mfma_kernel(SplitArgs a) {
   __shared__ MfmaShared<GP, NW> sh;
   if constexpr (MODE == kModePersistent) {
-    // Workgroup w first runs task w; further tasks (grid + k for the k-th
-    // claim) come from a device-scope counter, zeroed by the device planner
-    // and reset by the device merge, so they go to whichever workgroups are
-    // running.  A workgroup exits once its task index passes the task count
-    // (or at once after its first task when the grid covers every task), and
-    // none ever waits on another.
-    __shared__ int s_task;
-    const int n_tasks = a.device_plan[kNumTasks];
-    const int grid = static_cast<int>(gridDim.x);
-    int32_t* counter = a.device_plan + a.device_plan[kTotalWords];
-    int t = static_cast<int>(blockIdx.x);
-    while (t < n_tasks) {
-      mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, decode_task<kModeWorkqueue>(a, t), sh);
-      if (n_tasks <= grid) break;
-      __syncthreads();  // LDS (and s_task) are reused by the next task
-      if (threadIdx.x == 0) s_task = grid + atomicAdd(counter, 1);
-      __syncthreads();
-      t = s_task;
-    }
+    persistent_plan_loop(a, [&](const Task& tk) {
+      mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, tk, sh);
+    });
   } else if constexpr (MODE == kModeLens) {
-    // Same claim protocol as the persistent mode; the task list is the
-    // workqueue of the device lengths, rebuilt in LDS by every workgroup
-    // (O(B) work, B <= kMaxLensRows), and the counter is the caller's.
-    __shared__ int s_len[kMaxLensRows];
-    __shared__ int s_off[kMaxLensRows + 1];
-    __shared__ int s_red[NW];
-    __shared__ int s_task;
-    const int b = a.num_rows, hkv = a.num_kv_heads;
-    const int pps = __builtin_amdgcn_readfirstlane(lens_plan_in_lds<NW * 64>(
-        a.seq_lens, b, hkv, a.splits, int64_t(a.max_pages) * 16, s_len, s_off, s_red));
-    const int n_tasks = __builtin_amdgcn_readfirstlane(s_off[b]);
-    const int grid = static_cast<int>(gridDim.x);
-    int t = static_cast<int>(blockIdx.x);
-    while (t < n_tasks) {
-      mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, lens_task(t, s_len, s_off, b, hkv, pps), sh);
-      if (n_tasks <= grid) break;
-      __syncthreads();
-      if (threadIdx.x == 0) s_task = grid + atomicAdd(a.work_counter, 1);
-      __syncthreads();
-      t = __builtin_amdgcn_readfirstlane(s_task);
-    }
+    lens_loop<NW * 64>(a, [&](const Task& tk) {
+      mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, tk, sh);
+    });
   } else {
     const Task tk = decode_task<MODE>(a, blockIdx.x);
     if constexpr (MODE == kModeBucket) {

@@ -16,13 +16,17 @@
 // Method: PersistentKV summary pages, "Methodology / 1. Native block-table
 // decode engine" (GQA over paged KV read through the block table, partial
 // online-softmax state per disjoint split, empty splits write neutral state).
+#include "lens_plan.h"
 #include "split_common.h"
 
 namespace pkv {
 namespace {
 
+// One task (row, KV head, page range): stream its pages, then combine the
+// waves and write the partial state (or, no-split, the normalised output).
 template <int D, int GP, bool BF16, int NW, int PF, int MODE>
-__global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
+__device__ __forceinline__ void valu_task(const SplitArgs& a, Task tk, float (&sm_m)[NW][GP],
+                                          float (&sm_l)[NW][GP], float (&sm_o)[NW][GP][D]) {
   constexpr int CPT = D / 8;     // 16-byte chunks per token row
   constexpr int TPI = 64 / CPT;  // tokens per wave-wide 16-byte load
   constexpr int NL = 16 / TPI;   // loads per page (16 tokens per page)
@@ -33,18 +37,6 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
   const int hkv = a.num_kv_heads;
   const int G = a.num_q_heads / hkv;  // real heads in the group (<= GP)
 
-  __shared__ float sm_m[NW][GP];
-  __shared__ float sm_l[NW][GP];
-  __shared__ float sm_o[NW][GP][D];
-
-  // ---- task --------------------------------------------------------------
-  Task tk = decode_task<MODE>(a, blockIdx.x);
-  if constexpr (MODE == kModeBucket) {
-    if (tk.empty) {  // empty split: neutral state, exit early
-      write_neutral<NW>(a, tk, G, D);
-      return;
-    }
-  }
   const int row = tk.row, g = tk.g, pb = tk.page_begin;
   const int32_t* bt = a.block_table + int64_t(row) * a.max_pages;
   const int first = pb + wave;  // this wave's pages: first, first + NW, ...
@@ -220,6 +212,34 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
   combine_waves_and_store<D, GP, NW, BF16, MODE>(a, tk, G, sm_m, sm_l, sm_o);
 }
 
+// Grid modes as in the matrix-core kernel: one workgroup per workqueue task /
+// bucket slot / (row, KV head), or a persistent grid over a device-built plan
+// or over the workqueue each workgroup derives from the device lengths.
+template <int D, int GP, bool BF16, int NW, int PF, int MODE>
+__global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
+  __shared__ float sm_m[NW][GP];
+  __shared__ float sm_l[NW][GP];
+  __shared__ float sm_o[NW][GP][D];
+  if constexpr (MODE == kModePersistent) {
+    persistent_plan_loop(a, [&](const Task& tk) {
+      valu_task<D, GP, BF16, NW, PF, kModeWorkqueue>(a, tk, sm_m, sm_l, sm_o);
+    });
+  } else if constexpr (MODE == kModeLens) {
+    lens_loop<NW * 64>(a, [&](const Task& tk) {
+      valu_task<D, GP, BF16, NW, PF, kModeWorkqueue>(a, tk, sm_m, sm_l, sm_o);
+    });
+  } else {
+    const Task tk = decode_task<MODE>(a, blockIdx.x);
+    if constexpr (MODE == kModeBucket) {
+      if (tk.empty) {  // empty split: neutral state, exit early
+        write_neutral<NW>(a, tk, a.num_q_heads / a.num_kv_heads, D);
+        return;
+      }
+    }
+    valu_task<D, GP, BF16, NW, PF, MODE>(a, tk, sm_m, sm_l, sm_o);
+  }
+}
+
 template <int D, int GP, bool BF16, int NW, int PF>
 pkv_status launch_valu_modes(int mode, const SplitArgs& a, int grid, hipStream_t s) {
   const dim3 block(NW * 64);
@@ -232,8 +252,12 @@ pkv_status launch_valu_modes(int mode, const SplitArgs& a, int grid, hipStream_t
   else if (mode == kModeNoSplit)
     hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeNoSplit>), dim3(grid), block, 0,
                        s, a);
+  else if (mode == kModePersistent)
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModePersistent>), dim3(grid), block,
+                       0, s, a);
   else
-    return PKV_ESHAPE;
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeLens>), dim3(grid), block, 0, s,
+                       a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

@@ -278,10 +278,13 @@ def test_device_plan_entry_points_validate_before_launch():
     with pytest.raises(PkvError) as e:
         _lib.pkv_plan_device(wide, fake, 64, fake, need)
     assert e.value.status == PKV_ERANGE
-    with pytest.raises(PkvError) as e:  # d = 64 has no persistent kernel
-        _lib.pkv_decode_device(_prob(2, d=64), fake, 8, fake, fake, fake, fake, fake, fake, fake)
+    # Shapes no split kernel covers: d = 64 needs the vector-ALU kernel, which
+    # takes G <= 8; so does an explicit vector-ALU request.
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_decode_device(_prob(2, hq=32, hkv=2, d=64), fake, 8, fake, fake, fake, fake, fake,
+                               fake, fake)
     assert e.value.status == PKV_ESHAPE
-    valu = _prob(2)
+    valu = _prob(2, hq=32, hkv=2)
     valu.kernel = _lib.PKV_KERNEL_VALU
     with pytest.raises(PkvError) as e:
         _lib.pkv_decode_device(valu, fake, 8, fake, fake, fake, fake, fake, fake, fake)
@@ -310,10 +313,10 @@ def test_selfplan_entry_points_validate_before_launch():
     with pytest.raises(PkvError) as e:  # B * Hkv * S past 32-bit task indices
         _lib.pkv_decode_selfplan(_prob(1024, hq=4096, hkv=4096), fake, 65535, fake, *args)
     assert e.value.status == PKV_ERANGE
-    with pytest.raises(PkvError) as e:  # d = 64 has no persistent kernel
-        _lib.pkv_decode_selfplan(_prob(2, d=64), fake, 8, fake, *args)
+    with pytest.raises(PkvError) as e:  # d = 64 with G = 16: no split kernel covers it
+        _lib.pkv_decode_selfplan(_prob(2, hq=32, hkv=2, d=64), fake, 8, fake, *args)
     assert e.value.status == PKV_ESHAPE
-    valu = _prob(2)
+    valu = _prob(2, hq=32, hkv=2)  # the vector-ALU kernel takes G <= 8
     valu.kernel = _lib.PKV_KERNEL_VALU
     with pytest.raises(PkvError) as e:
         _lib.pkv_decode_selfplan(valu, fake, 8, fake, *args)

@@ -158,3 +158,32 @@ def test_selfplan_graph_capture_replays_with_growing_lengths():
         ref_out, ref_lse = oracle_out(w_k)
         check_out(step.out, ref_out, "f16", label=f"selfplan graph replay {k}")
         check_lse(step.lse, ref_lse, label=f"selfplan graph replay {k}")
+
+
+@pytest.mark.parametrize("d,kernel,hq,hkv", [(64, "auto", 8, 2), (64, "auto", 64, 8),
+                                              (128, "valu", 32, 8), (128, "valu", 16, 16)])
+def test_device_steps_on_the_vector_alu_kernel(d, kernel, hq, hkv):
+    """Both device-side steps (planned and self-planned) on the vector-ALU
+    kernel (d = 64, or asked for explicitly): against the oracle and bit for
+    bit against each other, with more tasks than the persistent grid."""
+    rng = np.random.default_rng(d + hq)
+    lens = rng.integers(0, 6000, size=24).astype(np.int32)
+    lens[::7] = 0
+    spec = traces.custom_spec(24, hq, hkv, d, splits=32, dtype="bf16" if hq == 64 else "f16")
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    say(f"[valu device steps] d={d} {kernel} hq={hq} hkv={hkv}")
+    wd = engine.to_device(w)
+    engine.validate_inputs(wd)
+    prob = engine.problem_from_workload(w, kernel)
+    steps = []
+    for cls in (engine.DeviceStep, engine.SelfPlannedStep):
+        st = cls(prob, 32)
+        st.run(wd)
+        torch.cuda.synchronize()
+        steps.append(st)
+    assert _same_bits(steps[0].out, steps[1].out) and _same_bits(steps[0].lse, steps[1].lse)
+    rows = sorted({0, 1, int(lens.argmax()), 23})
+    ref_out, ref_lse = oracle_out(w, rows=rows)
+    for st in steps:
+        check_out(st.out, ref_out, spec.dtype, rows=rows, label=f"valu {type(st).__name__}")
+        check_lse(st.lse, ref_lse, rows=rows, label=f"valu {type(st).__name__}")
