@@ -86,23 +86,14 @@ class DecodeStep:
         return self.out, self.lse
 
 
-class DeviceStep:
-    """Device-planned workqueue step: plan, split and merge all on the GPU.
-
-    ``run`` enqueues pkv_plan_device -> pkv_decode_device -> pkv_merge_device on
-    one stream with no host work, so the three launches can be captured once in
-    a HIP graph and replayed while the device lengths change.
-    """
+class _PersistentStepBuffers:
+    """Output and partial-state buffers of a persistent-grid workqueue step
+    (room for B * Hkv * S states: the most any length mix can need)."""
 
     def __init__(self, prob: _lib.pkv_problem, splits: int, device="cuda"):
         self.prob = prob
         self.splits = int(splits)
         self.device = torch.device(device)
-        nbytes = pkv_plan_bytes(prob, PKV_WORKQUEUE, self.splits)
-        if nbytes == 0:
-            raise _lib.PkvError("pkv_plan_bytes", _lib.PKV_EINVAL, "invalid problem")
-        self.plan_dev = torch.zeros(nbytes // 4, dtype=torch.int32, device=self.device)
-        self.bad_rows = torch.zeros(1, dtype=torch.int32, device=self.device)
         g = prob.num_q_heads // prob.num_kv_heads
         d = prob.head_dim
         dt = torch.bfloat16 if prob.dtype == _lib.PKV_BF16 else torch.float16
@@ -113,6 +104,23 @@ class DeviceStep:
         self.st_m = torch.empty(slots, g, dtype=torch.float32, device=self.device)
         self.st_l = torch.empty(slots, g, dtype=torch.float32, device=self.device)
         self.st_o = torch.empty(slots, g, d, dtype=torch.float32, device=self.device)
+
+
+class DeviceStep(_PersistentStepBuffers):
+    """Device-planned workqueue step: plan, split and merge all on the GPU.
+
+    ``run`` enqueues pkv_plan_device -> pkv_decode_device -> pkv_merge_device on
+    one stream with no host work, so the three launches can be captured once in
+    a HIP graph and replayed while the device lengths change.
+    """
+
+    def __init__(self, prob: _lib.pkv_problem, splits: int, device="cuda"):
+        super().__init__(prob, splits, device)
+        nbytes = pkv_plan_bytes(prob, PKV_WORKQUEUE, self.splits)
+        if nbytes == 0:
+            raise _lib.PkvError("pkv_plan_bytes", _lib.PKV_EINVAL, "invalid problem")
+        self.plan_dev = torch.zeros(nbytes // 4, dtype=torch.int32, device=self.device)
+        self.bad_rows = torch.zeros(1, dtype=torch.int32, device=self.device)
 
     def run(self, w: dict, stream=None):
         pkv_plan_device(self.prob, w["seq_lens"], self.splits, self.plan_dev,
@@ -125,7 +133,7 @@ class DeviceStep:
         return self.out, self.lse
 
 
-class SelfPlannedStep(DeviceStep):
+class SelfPlannedStep(_PersistentStepBuffers):
     """Self-planned workqueue step: the device-planned step in two launches.
 
     ``run`` enqueues pkv_decode_selfplan -> pkv_merge_selfplan: the split and
@@ -136,7 +144,6 @@ class SelfPlannedStep(DeviceStep):
 
     def __init__(self, prob: _lib.pkv_problem, splits: int, device="cuda"):
         super().__init__(prob, splits, device)
-        del self.plan_dev, self.bad_rows
         self.counter = torch.zeros(1, dtype=torch.int32, device=self.device)
 
     def run(self, w: dict, stream=None):
