@@ -79,3 +79,22 @@ def test_recorded_shape_checks():
     assert (sum(r["total_us"]["model"] for r in checks.values())
             <= sum(r["total_us"]["table"] for r in checks.values()))
 
+
+
+@pytest.mark.parametrize("name", ["cost_heldout_hq32_hkv2_f16.json",
+                                  "cost_heldout_hq32_hkv8_f16_d64.json"])
+def test_recorded_shape_checks_follow_from_the_stored_timings(name):
+    """Scoring the stored held-out timings again (model and table choices
+    through the C ABI) reproduces the recorded shape check exactly."""
+    import os
+
+    from paged_kv_gqa_block_amd import cost_fit
+
+    doc = _doc()
+    if name not in doc.get("shape_checks", {}):
+        pytest.skip("shape check not recorded")
+    path = os.path.join(os.path.dirname(engine.COST_MODEL_PATH), name)
+    again = cost_fit.evaluate_file(path, engine.COST_MODEL_PATH)
+    rec = doc["shape_checks"][name]
+    assert again["total_us"] == rec["total_us"]
+    assert again["cells_over_3pct"] == rec["cells_over_3pct"]
