@@ -13,6 +13,14 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kDepth = 2;  // pages of loads a wave keeps in flight
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal (streaming) cache policy.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // One workgroup per task; wave w reads the task's pages w, w + 4, ... two at a
 // time.  U = 16-byte loads per lane per page chunk (4 for d = 128, 2 for 64).
 template <int U>
@@ -32,9 +40,9 @@ __global__ __launch_bounds__(kWaves * 64) void probe_read_kernel(
       const int p = min(p0 + d, pe - 1);
       const int64_t base = (int64_t(bt_row[p]) * hkv + g) * (64 * U);
 #pragma unroll
-      for (int i = 0; i < U; ++i) {
-        buf[d][i] = k[base + i * 64 + lane];
-        buf[d][U + i] = v[base + i * 64 + lane];
+      for (int i = 0; i < U; ++i) {  // streaming (non-temporal) loads, as the split kernels
+        buf[d][i] = load_stream(k + base + i * 64 + lane);
+        buf[d][U + i] = load_stream(v + base + i * 64 + lane);
       }
     }
 #pragma unroll
