@@ -226,7 +226,9 @@ pkv_status pkv_plan_get_info(const pkv_problem* prob, const void* plan_host,
  * first T_i table entries of a row, are never used (they may hold NaN).
  * Errors: PKV_EINVAL, PKV_ESHAPE (shape or plan/problem mismatch),
  * PKV_EDTYPE, PKV_ERANGE (a launch of more than 2^24 - 1 workgroups: tasks,
- * B * Hkv for NOSPLIT, or rows_b * Hkv * S for one bucket), PKV_EHIP.
+ * B * Hkv for NOSPLIT, or rows_b * Hkv * S for one bucket; or a bucket of
+ * more than 65535 rows, the limit of its launch's third grid dimension),
+ * PKV_EHIP.
  */
 pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host, const void* plan_dev,
                       const void* q, const void* k_pool, const void* v_pool,

@@ -106,9 +106,11 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
   // length from the plan's row_len array (bucket length word -1).
   a.row_len = dev + PKV_PLAN_HEADER_WORDS;
   const int32_t* bw = w + w[kOffBuckets];
-  for (int k = 0; k < w[kNumBuckets]; ++k)  // every launch size, before the first launch
-    if (int64_t(bw[kBucketWords * k + 4]) * prob->num_kv_heads * w[kSplits] > kMaxGridGroups)
+  for (int k = 0; k < w[kNumBuckets]; ++k) {  // every launch size, before the first launch
+    const int64_t rows = bw[kBucketWords * k + 4];
+    if (rows > kMaxBucketRows || rows * prob->num_kv_heads * w[kSplits] > kMaxGridGroups)
       return PKV_ERANGE;
+  }
   for (int k = 0; k < w[kNumBuckets]; ++k) {
     const int32_t* e = bw + kBucketWords * k;
     const int64_t items = int64_t(e[4]) * prob->num_kv_heads * w[kSplits];

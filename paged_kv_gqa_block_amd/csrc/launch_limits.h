@@ -10,4 +10,8 @@ namespace pkv {
 // uses more than 256 threads per workgroup.
 constexpr int64_t kMaxGridGroups = (int64_t(1) << 24) - 1;
 
+// Largest row count of one bucket launch: the rows are the third grid
+// dimension, whose size HIP bounds by 65535 workgroups.
+constexpr int64_t kMaxBucketRows = 65535;
+
 }  // namespace pkv

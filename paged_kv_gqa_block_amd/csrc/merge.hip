@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int ri = item / a.num_q_heads;
   const int h = item - ri * a.num_q_heads;
   const int hkv = a.num_kv_heads;
-  const int G = a.num_q_heads / hkv;
+  const int G = a.group;
   const int g = h / G;
   const int hh = h - g * G;
   int row, nsplit;
@@ -143,7 +143,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 }  // namespace
 
-pkv_status launch_merge(const pkv_problem& p, const MergeArgs& a, hipStream_t s) {
+pkv_status launch_merge(const pkv_problem& p, const MergeArgs& args, hipStream_t s) {
+  MergeArgs a = args;
+  a.group = p.num_q_heads / p.num_kv_heads;
   const int64_t items = int64_t(a.num_rows) * p.num_q_heads;
   if (items == 0) return PKV_OK;
   if (items > kMaxGridGroups) return PKV_ERANGE;
@@ -168,9 +170,11 @@ pkv_status launch_split_mfma(const pkv_problem& p, int mode, const SplitArgs& a,
 // wherever it applies (d = 128, any G <= 16) -- on MI355X it is faster than the
 // vector-ALU kernel on every measured workload -- and the vector-ALU kernel for
 // d = 64 (G <= 8).  Every grid mode exists in both kernels.
-pkv_status launch_split(const pkv_problem& p, int mode, int kernel, const SplitArgs& a, int grid,
-                        hipStream_t s) {
+pkv_status launch_split(const pkv_problem& p, int mode, int kernel, const SplitArgs& args,
+                        int grid, hipStream_t s) {
   if (grid <= 0) return PKV_OK;
+  SplitArgs a = args;
+  a.group = p.num_q_heads / p.num_kv_heads;
   if (kernel == PKV_KERNEL_MFMA || (kernel == PKV_KERNEL_AUTO && p.head_dim == 128))
     return launch_split_mfma(p, mode, a, grid, s);
   return launch_split_valu(p, mode, a, grid, s);

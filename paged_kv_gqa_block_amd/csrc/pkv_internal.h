@@ -120,6 +120,7 @@ struct SplitArgs {
   float* lse;   // no-split, may be null
   int32_t num_q_heads;
   int32_t num_kv_heads;
+  int32_t group;      // G = Hq / Hkv, set by launch_split (no division on the device)
   int32_t max_pages;  // block-table row stride
   int32_t splits;     // bucket: S (slot stride)
   int32_t bucket_pps;
@@ -145,6 +146,7 @@ struct MergeArgs {
   float* lse;
   int32_t num_q_heads;
   int32_t num_kv_heads;
+  int32_t group;      // G = Hq / Hkv, set by launch_merge
   int32_t splits;     // bucket slot stride S
   int32_t num_rows;   // rows covered by this launch
   int32_t mode;       // kModeWorkqueue or kModeBucket

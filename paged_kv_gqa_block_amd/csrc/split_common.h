@@ -33,10 +33,13 @@ __device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
     t.tok_end = w.w;
     t.slot = item;
   } else if constexpr (MODE == kModeBucket) {
-    const int s = item % a.splits;
-    const int rest = item / a.splits;
-    t.g = rest % hkv;
-    t.row = (a.bucket_row0 >= 0) ? a.bucket_row0 : a.bucket_rows[rest / hkv];
+    // Three-dimensional grid (split slot, KV head, row of the bucket): the
+    // task comes from the block index without an integer division, so the
+    // block-table read is issued a few hundred scalar instructions earlier.
+    (void)item;
+    const int s = blockIdx.x;
+    t.g = blockIdx.y;
+    t.row = (a.bucket_row0 >= 0) ? a.bucket_row0 : a.bucket_rows[blockIdx.z];
     t.slot = (int64_t(t.row) * hkv + t.g) * a.splits + s;
     // Exact bucket: the rows share length, pages and split count.  Padded
     // bucket: the row's own length bounds its splits (row-local bounds).
@@ -57,6 +60,14 @@ __device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
     t.tok_end = -1;  // filled in from seq_lens by the caller
   }
   return t;
+}
+
+// Grid of one bucket launch: (split slot, KV head, row of the bucket); the
+// host keeps the row count within kMaxBucketRows.
+inline dim3 bucket_grid(const SplitArgs& a, int items) {
+  const int per_row = a.splits * a.num_kv_heads;
+  return dim3(static_cast<uint32_t>(a.splits), static_cast<uint32_t>(a.num_kv_heads),
+              static_cast<uint32_t>(items / per_row));
 }
 
 // Persistent grid over a device-built workqueue plan: workgroup w first runs

@@ -109,8 +109,11 @@ struct Pv<false> {  // fp16 P and V
 
 template <>
 struct Pv<true> {  // bf16 P and V
+  // One v_cvt_pk_bf16_f32 (gfx950): both values rounded to nearest even, the
+  // default rounding mode.  P is finite, so no NaN handling is needed here.
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return uint32_t(Elem<true>::from_float(a)) | (uint32_t(Elem<true>::from_float(b)) << 16);
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf162_t));
   }
   static __device__ __forceinline__ float lo(uint32_t w) { return Elem<true>::lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return Elem<true>::hi(w); }
@@ -141,7 +144,7 @@ __device__ __forceinline__ void mfma_task(const SplitArgs& a, Task tk, MfmaShare
   const int c = lane & 15;   // element chunk [8c, 8c+8); also MFMA column n / head m
   const int kg = lane >> 4;  // row group: tokens kg + 4i
   const int hkv = a.num_kv_heads;
-  const int G = a.num_q_heads / hkv;
+  const int G = a.group;
   auto& sm_m = sh.m;
   auto& sm_l = sh.l;
   auto& sm_o = sh.o;
@@ -339,7 +342,7 @@ void split_mfma_kernel(SplitArgs a) {
     const Task tk = decode_task<MODE>(a, blockIdx.x);
     if constexpr (MODE == kModeBucket) {
       if (tk.empty) {  // empty split: neutral state, exit early
-        write_neutral<NW>(a, tk, a.num_q_heads / a.num_kv_heads, 128);
+        write_neutral<NW>(a, tk, a.group, 128);
         return;
       }
     }
@@ -354,8 +357,7 @@ pkv_status launch_mfma_modes(int mode, const SplitArgs& a, int grid, hipStream_t
     hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeWorkqueue>), dim3(grid), block, 0,
                        s, a);
   else if (mode == kModeBucket)
-    hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeBucket>), dim3(grid), block, 0, s,
-                       a);
+    hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeBucket>), bucket_grid(a, grid), block, 0, s, a);
   else if (mode == kModeNoSplit)
     hipLaunchKernelGGL((split_mfma_kernel<GP, BF16, NW, PF, kModeNoSplit>), dim3(grid), block, 0,
                        s, a);

@@ -35,7 +35,7 @@ __device__ __forceinline__ void valu_task(const SplitArgs& a, Task tk, float (&s
   const int c = lane % CPT;  // chunk: elements [8c, 8c+8)
   const int r = lane / CPT;  // stream: tokens r, r+TPI, ... of each page
   const int hkv = a.num_kv_heads;
-  const int G = a.num_q_heads / hkv;  // real heads in the group (<= GP)
+  const int G = a.group;  // real heads in the group (<= GP)
 
   const int row = tk.row, g = tk.g, pb = tk.page_begin;
   const int32_t* bt = a.block_table + int64_t(row) * a.max_pages;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
     const Task tk = decode_task<MODE>(a, blockIdx.x);
     if constexpr (MODE == kModeBucket) {
       if (tk.empty) {  // empty split: neutral state, exit early
-        write_neutral<NW>(a, tk, a.num_q_heads / a.num_kv_heads, D);
+        write_neutral<NW>(a, tk, a.group, D);
         return;
       }
     }
@@ -247,8 +247,7 @@ pkv_status launch_valu_modes(int mode, const SplitArgs& a, int grid, hipStream_t
     hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeWorkqueue>), dim3(grid), block, 0,
                        s, a);
   else if (mode == kModeBucket)
-    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeBucket>), dim3(grid), block, 0, s,
-                       a);
+    hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeBucket>), bucket_grid(a, grid), block, 0, s, a);
   else if (mode == kModeNoSplit)
     hipLaunchKernelGGL((split_valu_kernel<D, GP, BF16, NW, PF, kModeNoSplit>), dim3(grid), block, 0,
                        s, a);
