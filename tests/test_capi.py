@@ -247,6 +247,14 @@ def test_launches_past_the_dispatch_limit_are_rejected_before_launch():
     with pytest.raises(PkvError) as e:
         _lib.pkv_decode(prob, buf, fake, fake, fake, fake, fake, fake, fake, fake, fake)
     assert e.value.status == PKV_ERANGE
+    # Bucketed decode: a bucket's rows are its launch's third grid dimension,
+    # at most 65535, even when the slot count is far below the limit.
+    prob = _prob(65536, hq=1, hkv=1, max_pages=4)
+    buf = _plan_buf(prob, np.full(65536, 16, np.int32), PKV_BUCKETED, 1)
+    assert 65536 * 1 * 1 <= limit
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_decode(prob, buf, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ERANGE
 
 
 def test_status_strings():
