@@ -5,6 +5,7 @@
 // uses hand-calibrated thresholds instead).  Host code only; it allocates
 // nothing (bucket orders use the caller's scratch, per-CU sums the stack).
 #include <algorithm>
+#include <cstdint>
 #include <cmath>
 
 #include "pkv_internal.h"
@@ -16,19 +17,59 @@ namespace {
 constexpr int kMaxCus = 1024;
 
 // Per-CU load of one launch: grid item j goes to CU j mod num_cus (the
-// round-robin spread of a launch's workgroups); returns the largest sum of
-// pages over the CUs.
+// round-robin spread of a launch's workgroups); max() is the largest sum of
+// pages over the CUs.  The items of one (row, KV head) are a run of
+// consecutive grid items, all of `pps` pages except the last (`last` pages),
+// possibly followed by empty bucket slots.  A run is added in O(1): whole
+// turns around the CUs go to a common offset, the rest to a difference array
+// over the CUs, and the last item's shortfall to a point correction; max()
+// then costs O(num_cus).  The sums are exactly those of adding the items one
+// by one.
 struct CuLoad {
-  int64_t acc[kMaxCus];
+  int64_t diff[kMaxCus + 1];
+  int64_t point[kMaxCus];
+  int64_t base;  // pages added to every CU
   int32_t cus;
-  int64_t j;
+  int32_t k;     // CU of the next grid item
+  int64_t j;     // grid items so far
   void start(int32_t n) {
     cus = n;
+    k = 0;
     j = 0;
-    std::fill(acc, acc + n, 0);
+    base = 0;
+    std::fill(diff, diff + n + 1, 0);
+    std::fill(point, point + n, 0);
   }
-  void add(int64_t pages) { acc[j++ % cus] += pages; }
-  int64_t max() const { return *std::max_element(acc, acc + cus); }
+  // `n` items of `pps` pages at CUs k, k+1, ... (mod cus), the last one of
+  // `last` pages (n >= 1, last <= pps), then `advance` - n empty items.
+  void add_run(int64_t n, int64_t pps, int64_t last, int64_t advance) {
+    base += (n / cus) * pps;
+    const int64_t r = n % cus;
+    if (r > 0) {
+      const int64_t end = k + r;
+      diff[k] += pps;
+      if (end <= cus) {
+        diff[end] -= pps;
+      } else {
+        diff[cus] -= pps;
+        diff[0] += pps;
+        diff[end - cus] -= pps;
+      }
+    }
+    point[(k + n - 1) % cus] -= pps - last;
+    k = static_cast<int32_t>((k + advance) % cus);
+    j += advance;
+  }
+  // One item of `pages` pages.
+  void add(int64_t pages) { add_run(1, pages, pages, 1); }
+  int64_t max() const {
+    int64_t run = 0, best = INT64_MIN;
+    for (int32_t c = 0; c < cus; ++c) {
+      run += diff[c];
+      best = std::max(best, base + run + point[c]);
+    }
+    return best;
+  }
 };
 
 pkv_status features(const pkv_problem* prob, const int32_t* lens, int32_t path, int32_t splits,
@@ -45,15 +86,16 @@ pkv_status features(const pkv_problem* prob, const int32_t* lens, int32_t path, 
   const PlanCounts c = count_plan(*prob, lens, path, splits, bucketed ? scratch : nullptr);
 
   // Grid items in launch order with their pages (0 for an empty slot).
-  CuLoad load;  // 8 KiB on the stack
+  CuLoad load;  // 16 KiB on the stack
   int64_t crit = 0, items = 0;
   load.start(num_cus);
   if (path == PKV_WORKQUEUE) {
     for (int32_t i = 0; i < b; ++i) {
       const int64_t t = ceil_div(lens[i], psz);
       const int64_t ns = ceil_div(t, c.pps);
-      for (int32_t g = 0; g < hkv; ++g)
-        for (int64_t s = 0; s < ns; ++s) load.add(std::min<int64_t>(c.pps, t - s * c.pps));
+      if (ns == 0) continue;
+      const int64_t last = t - (ns - 1) * c.pps;
+      for (int32_t g = 0; g < hkv; ++g) load.add_run(ns, c.pps, last, ns);
     }
     items = load.j;
     crit = load.max();
@@ -69,9 +111,15 @@ pkv_status features(const pkv_problem* prob, const int32_t* lens, int32_t path, 
                       load.start(num_cus);
                       for (int32_t r = first; r < end; ++r) {
                         const int64_t t = ceil_div(lens[scratch[r]], psz);
-                        for (int32_t g = 0; g < hkv; ++g)
-                          for (int32_t s = 0; s < splits; ++s)
-                            load.add(std::max<int64_t>(0, std::min<int64_t>(pps, t - int64_t(s) * pps)));
+                        const int64_t ns = std::min<int64_t>(ceil_div(t, pps), splits);
+                        for (int32_t g = 0; g < hkv; ++g) {
+                          if (ns == 0) {  // every slot of the row is empty
+                            load.add_run(1, 0, 0, splits);
+                          } else {
+                            load.add_run(ns, pps, std::min<int64_t>(pps, t - (ns - 1) * pps),
+                                         splits);
+                          }
+                        }
                       }
                       items += load.j;
                       crit += load.max();
