@@ -34,8 +34,8 @@ __device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
     t.slot = item;
   } else if constexpr (MODE == kModeBucket) {
     // Three-dimensional grid (split slot, KV head, row of the bucket): the
-    // task comes from the block index without an integer division, so the
-    // block-table read is issued a few hundred scalar instructions earlier.
+    // task comes from the block index without the integer divisions (a few
+    // dozen scalar instructions each) that a 1-D index would need.
     (void)item;
     const int s = blockIdx.x;
     t.g = blockIdx.y;
