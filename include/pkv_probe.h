@@ -7,7 +7,8 @@
  * (row, kv_head, page_begin, token_end) the pages
  * block_table[row][page_begin .. ceil(token_end / P)) of head kv_head, whole
  * pages of P * head_dim elements, with no arithmetic beyond folding the loaded
- * words into one register.  Timing it gives the HBM rate that this exact
+ * words into one register.  The loads carry the non-temporal (streaming)
+ * cache policy, as the split kernel's KV loads do.  Timing it gives the HBM rate that this exact
  * access pattern (random 16-token pages of one KV head, as laid out in the
  * [pages][Hkv][P][d] pools) reaches on the device, the practical ceiling of
  * the split kernel for that workload.  The method's access pattern is the
