@@ -29,13 +29,19 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int t = threadIdx.x;
   const int ch = t % CH;
   const int sg = t / CH;
-  const int item = blockIdx.x;  // (row index, q head)
+  // Item = (row index, query head), KV head fastest within a row: item j of
+  // a row is query head hh = j / Hkv of KV head g = j % Hkv.  Workgroups go to
+  // the 8 XCDs round-robin, so with Hq and Hkv multiples of 8 the merge of a
+  // KV head runs on the XCD where a bucket launch ran all of that head's
+  // splits (split_common.h), and reads their states from that XCD's L2.
+  const int item = blockIdx.x;
   const int ri = item / a.num_q_heads;
-  const int h = item - ri * a.num_q_heads;
+  const int j = item - ri * a.num_q_heads;
   const int hkv = a.num_kv_heads;
   const int G = a.group;
-  const int g = h / G;
-  const int hh = h - g * G;
+  const int g = j % hkv;
+  const int hh = j / hkv;
+  const int h = g * G + hh;
   int row, nsplit;
   int64_t base;  // first state slot of this (row, kv head)
   __shared__ int s_red[4];

@@ -33,12 +33,12 @@ __device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
     t.tok_end = w.w;
     t.slot = item;
   } else if constexpr (MODE == kModeBucket) {
-    // Three-dimensional grid (split slot, KV head, row of the bucket): the
+    // Three-dimensional grid (KV head, split slot, row of the bucket): the
     // task comes from the block index without the integer divisions (a few
     // dozen scalar instructions each) that a 1-D index would need.
     (void)item;
-    const int s = blockIdx.x;
-    t.g = blockIdx.y;
+    t.g = blockIdx.x;
+    const int s = blockIdx.y;
     t.row = (a.bucket_row0 >= 0) ? a.bucket_row0 : a.bucket_rows[blockIdx.z];
     t.slot = (int64_t(t.row) * hkv + t.g) * a.splits + s;
     // Exact bucket: the rows share length, pages and split count.  Padded
@@ -62,11 +62,15 @@ __device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
   return t;
 }
 
-// Grid of one bucket launch: (split slot, KV head, row of the bucket); the
-// host keeps the row count within kMaxBucketRows.
+// Grid of one bucket launch: (KV head, split slot, row of the bucket), KV
+// head fastest.  Workgroups are dealt to the 8 XCDs round-robin in launch
+// order, so with Hkv a multiple of 8 every split of one KV head runs on one
+// XCD; the merge puts that head's query heads on the same XCD (merge.hip),
+// where its L2 still holds the states.  The host keeps the row count within
+// kMaxBucketRows.
 inline dim3 bucket_grid(const SplitArgs& a, int items) {
   const int per_row = a.splits * a.num_kv_heads;
-  return dim3(static_cast<uint32_t>(a.splits), static_cast<uint32_t>(a.num_kv_heads),
+  return dim3(static_cast<uint32_t>(a.num_kv_heads), static_cast<uint32_t>(a.splits),
               static_cast<uint32_t>(items / per_row));
 }
 
