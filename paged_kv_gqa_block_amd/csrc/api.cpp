@@ -93,6 +93,16 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
     if (n > kMaxGridGroups) return PKV_ERANGE;
     a.tasks = dev + w[kOffTasks];
     a.num_items = n;
+    // XCD-affine launch order (launch_item in split_common.h) when every row
+    // has the same split count u, the tasks are exactly B * Hkv * u and
+    // B * Hkv is a multiple of 8.
+    const int b = prob->batch;
+    const int32_t* ns = w + PKV_PLAN_HEADER_WORDS + 2 * b;
+    int32_t u = ns[0];
+    for (int r = 1; r < b && u > 0; ++r)
+      if (ns[r] != u) u = 0;
+    const int64_t pairs = int64_t(b) * prob->num_kv_heads;
+    a.xcd_nsplit = (u > 0 && pairs % 8 == 0 && pairs * u == n) ? u : 0;
     return launch_split(*prob, kModeWorkqueue, prob->kernel, a, n, stream);
   }
   if (path == PKV_NOSPLIT) {

@@ -130,6 +130,8 @@ struct SplitArgs {
                         // they differ (padded bucket: lengths from row_len)
   int32_t bucket_row0;  // bucket: its only row when it has one, else -1
   int32_t num_items;    // grid items (tasks, bucket slots or rows * Hkv)
+  int32_t xcd_nsplit;   // workqueue: the split count every row shares when the
+                        // XCD-affine launch order applies (launch_item), else 0
   float scale_log2;   // sm_scale * log2(e)
   int32_t num_rows;        // lens mode: B
   int32_t* work_counter;   // lens mode: task claim counter (zero between steps)

@@ -62,6 +62,27 @@ __device__ __forceinline__ Task decode_task(const SplitArgs& a, int item) {
   return t;
 }
 
+// Task index of this workgroup in a one-workgroup-per-item launch.  A
+// workqueue launch whose rows all have ns splits, with B * Hkv a multiple of 8
+// (a.xcd_nsplit = ns, checked on the host), deals whole (row, KV head) pairs
+// to the 8 XCDs: block j (XCD j mod 8) runs task p * ns + (j / 8) mod ns of
+// pair p = 8 * ((j / 8) / ns) + j mod 8.  This is a bijection on the tasks,
+// and every split of pair p runs on XCD p mod 8, where the merge of that KV
+// head runs (merge.hip).  Other launches run task j.
+template <int MODE>
+__device__ __forceinline__ int launch_item(const SplitArgs& a) {
+  const int j = static_cast<int>(blockIdx.x);
+  if constexpr (MODE == kModeWorkqueue) {
+    const int ns = a.xcd_nsplit;
+    if (ns > 0) {
+      const int k = j >> 3;
+      const int q = k / ns;
+      return ((q << 3) + (j & 7)) * ns + (k - q * ns);
+    }
+  }
+  return j;
+}
+
 // Grid of one bucket launch: (KV head, split slot, row of the bucket), KV
 // head fastest.  Workgroups are dealt to the 8 XCDs round-robin in launch
 // order, so with Hkv a multiple of 8 every split of one KV head runs on one

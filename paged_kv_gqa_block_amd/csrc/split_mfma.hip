@@ -339,7 +339,7 @@ void split_mfma_kernel(SplitArgs a) {
       mfma_task<GP, BF16, NW, PF, kModeWorkqueue>(a, tk, sh);
     });
   } else {
-    const Task tk = decode_task<MODE>(a, blockIdx.x);
+    const Task tk = decode_task<MODE>(a, launch_item<MODE>(a));
     if constexpr (MODE == kModeBucket) {
       if (tk.empty) {  // empty split: neutral state, exit early
         write_neutral<NW>(a, tk, a.group, 128);

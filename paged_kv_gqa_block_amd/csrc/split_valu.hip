@@ -229,7 +229,7 @@ __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
       valu_task<D, GP, BF16, NW, PF, kModeWorkqueue>(a, tk, sm_m, sm_l, sm_o);
     });
   } else {
-    const Task tk = decode_task<MODE>(a, blockIdx.x);
+    const Task tk = decode_task<MODE>(a, launch_item<MODE>(a));
     if constexpr (MODE == kModeBucket) {
       if (tk.empty) {  // empty split: neutral state, exit early
         write_neutral<NW>(a, tk, a.group, D);

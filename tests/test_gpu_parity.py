@@ -273,7 +273,9 @@ def test_random_small_problems_every_path(seed):
 def test_workqueue_merge_with_shared_and_mixed_split_counts(lens):
     """The workqueue merge locates a row's states from its index when every
     row has the same split count, and from the plan's row arrays otherwise:
-    both against the oracle, on both kernels' states."""
+    both against the oracle, on both kernels' states.  With a shared split
+    count (B * Hkv = 32 pairs) the split launch also takes its XCD-affine
+    task order."""
     lens = np.asarray(lens, dtype=np.int32)
     spec = traces.custom_spec(4, 32, 8, 128, splits=8, dtype="f16")
     w = traces.generate(spec, SEED, seq_lens=lens)
@@ -301,3 +303,22 @@ def test_large_batch_short_contexts_every_path():
         check_out(step.out, ref_out, "bf16", rows=rows, label=f"large/{path}")
         check_lse(step.lse, ref_lse, rows=rows, label=f"large/{path}")
         assert torch.isfinite(step.out.float()).all()
+
+
+@pytest.mark.parametrize("hq,hkv,b,n", [(16, 4, 2, 700), (8, 1, 8, 333), (32, 8, 3, 1000)])
+def test_workqueue_xcd_launch_order(hq, hkv, b, n):
+    """Equal lengths give every row the same split count, and B * Hkv is a
+    multiple of 8 (8, 8 and 24 pairs), so the split launch takes its
+    XCD-affine task order (a permutation of the tasks over the blocks).  With
+    Hkv = 4 or 1 a KV head's splits and its merge sit on different XCDs, which
+    changes nothing in the results: every case matches the oracle on both
+    kernels."""
+    lens = np.full(b, n, dtype=np.int32)
+    spec = traces.custom_spec(b, hq, hkv, 128, splits=16, dtype="bf16")
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    say(f"[wq xcd] hq={hq} hkv={hkv} b={b} n={n}")
+    ref_out, ref_lse = oracle_out(w)
+    for kernel in KERNELS:
+        step, _ = _run(w, "workqueue", 16, kernel)
+        check_out(step.out, ref_out, "bf16", label=f"wqxcd/{kernel}")
+        check_lse(step.lse, ref_lse, label=f"wqxcd/{kernel}")
