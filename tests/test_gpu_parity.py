@@ -322,3 +322,33 @@ def test_workqueue_xcd_launch_order(hq, hkv, b, n):
         step, _ = _run(w, "workqueue", 16, kernel)
         check_out(step.out, ref_out, "bf16", label=f"wqxcd/{kernel}")
         check_lse(step.lse, ref_lse, label=f"wqxcd/{kernel}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_equal_split_counts_every_split_path(seed):
+    """Random head shapes, batch sizes, split caps and dtypes with lengths
+    drawn so that every row gets the same split count: the workqueue launch
+    takes its XCD-affine order whenever B * Hkv is a multiple of 8, and bucket
+    launches their (KV head, split, row) grid.  Every split path on both
+    kernels against the oracle."""
+    rng = np.random.default_rng(7100 + seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    b = int(rng.choice([1, 2, 4, 8, 16])) if seed % 2 == 0 else int(rng.integers(1, 17))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    splits = int(rng.choice([2, 5, 8, 16, 32]))
+    tmax = int(rng.integers(1, 200))  # pages of the longest row
+    pps = max(1, -(-tmax // splits))  # the batch-shared granule
+    ns = -(-tmax // pps)
+    pages = rng.integers((ns - 1) * pps + 1, tmax + 1, size=b)
+    pages[0] = tmax
+    lens = ((pages - 1) * 16 + rng.integers(1, 17, size=b)).astype(np.int32)
+    spec = traces.custom_spec(b, hkv * g, hkv, 128, splits=splits, dtype=dtype)
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    say(f"[equal splits {seed}] B={b} Hq={hkv * g} Hkv={hkv} S={splits} ns={ns} {dtype}")
+    ref_out, ref_lse = oracle_out(w)
+    for kernel in KERNELS:
+        for path in ("workqueue", "bucketed", "padded"):
+            step, _ = _run(w, path, splits, kernel)
+            check_out(step.out, ref_out, dtype, label=f"equal{seed}/{kernel}/{path}")
+            check_lse(step.lse, ref_lse, label=f"equal{seed}/{kernel}/{path}")
