@@ -21,12 +21,12 @@ __device__ __forceinline__ int lens_valid(int n, int64_t cap) { return (n < 0 ||
 // Every workgroup of the split kernel builds the row offsets of the task list
 // in LDS: s_len[r] = N_r (invalid lengths as 0), s_off[r] = first task of row
 // r, s_off[B] = task count.  NT threads, each owning up to kMaxLensRows / NT
-// consecutive rows; s_red holds one int per wave.  Returns pps.  Ends with a
-// barrier.
+// consecutive rows; s_red holds one int per wave.  Returns pps, and in
+// *ns_max the split count of the longest row.  Ends with a barrier.
 template <int NT>
 __device__ __forceinline__ int lens_plan_in_lds(const int32_t* __restrict__ seq_lens, int b,
                                                 int hkv, int splits, int64_t cap, int* s_len,
-                                                int* s_off, int* s_red) {
+                                                int* s_off, int* s_red, int* ns_max) {
   constexpr int kPer = kMaxLensRows / NT;
   constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -45,6 +45,7 @@ __device__ __forceinline__ int lens_plan_in_lds(const int32_t* __restrict__ seq_
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) t_max = max(t_max, s_red[w]);
   const int pps = max(1, (t_max + splits - 1) / splits);
+  *ns_max = (t_max + pps - 1) / pps;
   int local = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) local += hkv * ((((n[i] + 15) >> 4) + pps - 1) / pps);
@@ -111,11 +112,24 @@ __device__ __forceinline__ void lens_loop(const SplitArgs& a, RunTask run) {
   __shared__ int s_red[NT / 64];
   __shared__ int s_task;
   const int b = a.num_rows, hkv = a.num_kv_heads;
+  int ns_max;
   const int pps = __builtin_amdgcn_readfirstlane(lens_plan_in_lds<NT>(
-      a.seq_lens, b, hkv, a.splits, int64_t(a.max_pages) * 16, s_len, s_off, s_red));
+      a.seq_lens, b, hkv, a.splits, int64_t(a.max_pages) * 16, s_len, s_off, s_red, &ns_max));
+  ns_max = __builtin_amdgcn_readfirstlane(ns_max);
   const int n_tasks = __builtin_amdgcn_readfirstlane(s_off[b]);
   const int grid = static_cast<int>(gridDim.x);
   int t = static_cast<int>(blockIdx.x);
+  // When the grid covers every task (one task per workgroup) and every row
+  // has the longest row's split count, with B * Hkv a multiple of 8, the
+  // first task follows the XCD-affine order of launch_item (split_common.h):
+  // a bijection on [0, n_tasks) that runs each (row, KV head)'s splits on
+  // the XCD of its merge.
+  if (t < n_tasks && n_tasks <= grid && ns_max > 0 && (b * hkv) % 8 == 0 &&
+      n_tasks == b * hkv * ns_max) {
+    const int k = t >> 3;
+    const int q = k / ns_max;
+    t = ((q << 3) + (t & 7)) * ns_max + (k - q * ns_max);
+  }
   while (t < n_tasks) {
     run(lens_task(t, s_len, s_off, b, hkv, pps));
     if (n_tasks <= grid) break;

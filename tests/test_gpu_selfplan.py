@@ -187,3 +187,40 @@ def test_device_steps_on_the_vector_alu_kernel(d, kernel, hq, hkv):
     for st in steps:
         check_out(st.out, ref_out, spec.dtype, rows=rows, label=f"valu {type(st).__name__}")
         check_lse(st.lse, ref_lse, rows=rows, label=f"valu {type(st).__name__}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_selfplan_equal_split_counts(seed):
+    """Every row with the same split count and B * Hkv a multiple of 8 (most
+    draws): the self-planned grid starts each workgroup on a task of the
+    XCD-affine order.  States and outputs equal the host-planned workqueue's
+    bit for bit (same tasks, same slots, same task body), and the output
+    matches the oracle."""
+    rng = np.random.default_rng(8200 + seed)
+    hkv = int(rng.choice([2, 4, 8]))
+    g = int(rng.choice([1, 4, 8]))
+    b = int(rng.choice([1, 2, 4, 8, 12]))
+    s = int(rng.choice([4, 16, 32]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    tmax = int(rng.integers(2, 300))
+    pps = max(1, -(-tmax // s))
+    ns = -(-tmax // pps)
+    pages = rng.integers((ns - 1) * pps + 1, tmax + 1, size=b)
+    pages[0] = tmax
+    lens = ((pages - 1) * 16 + rng.integers(1, 17, size=b)).astype(np.int32)
+    spec = traces.custom_spec(b, hkv * g, hkv, 128, splits=s, dtype=dtype)
+    w = traces.generate(spec, SEED + seed, seq_lens=lens)
+    say(f"[selfplan equal splits] seed={seed} B={b} Hkv={hkv} G={g} S={s} ns={ns} {dtype}")
+    sp, wd = _run(engine.SelfPlannedStep, w, s)
+    host = engine.DecodeStep(engine.problem_from_workload(w), "workqueue", s)
+    info = host.plan(wd["seq_lens_host"])
+    host.run(wd)
+    torch.cuda.synchronize()
+    n_tasks = int(info.n_tasks)
+    assert n_tasks == b * hkv * ns
+    for name in ("st_m", "st_l", "st_o"):
+        assert _same_bits(getattr(sp, name)[:n_tasks], getattr(host, name)[:n_tasks]), name
+    assert _same_bits(sp.out, host.out) and _same_bits(sp.lse, host.lse)
+    ref_out, ref_lse = oracle_out(w)
+    check_out(sp.out, ref_out, dtype, label=f"selfplan-equal {seed}")
+    check_lse(sp.lse, ref_lse, label=f"selfplan-equal {seed}")
