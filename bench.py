@@ -106,6 +106,20 @@ def recorded_traffic(config: str, kernel_used: str, path: str, splits: int, seed
     return int(fields["traffic_bytes_per_launch"].strip())
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, budget_s):
     import numpy as np
 
@@ -137,7 +151,7 @@ def cpu_baseline(w, budget_s):
             break
     dt = time.perf_counter() - t0
     return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"fp64 numpy oracle on the same {spec.name} inputs: {reps} pass(es) over "
                       f"rows in order, {done_bytes / 1e6:.1f} MB of real KV in {dt:.1f} s "
                       f"({os.cpu_count()} host cpus visible)",

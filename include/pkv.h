@@ -224,6 +224,8 @@ pkv_status pkv_plan_get_info(const pkv_problem* prob, const void* plan_host,
  *     and may be NULL.  Rows with N_i = 0 get out = 0, lse = -inf.
  * Tokens past N_i in a row's last page, and pool pages not referenced by the
  * first T_i table entries of a row, are never used (they may hold NaN).
+ * Every path takes the row lengths N_i from the plan (the lengths pkv_plan
+ * validated); seq_lens_dev is not read and may be NULL.
  * Errors: PKV_EINVAL, PKV_ESHAPE (shape or plan/problem mismatch),
  * PKV_EDTYPE, PKV_ERANGE (a launch of more than 2^24 - 1 workgroups: tasks,
  * B * Hkv for NOSPLIT, or rows_b * Hkv * S for one bucket; or a bucket of
@@ -251,7 +253,8 @@ pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void*
 
 /*
  * Learned cost model (an alternative to the threshold table; the pages leave
- * a learned model as future work, "Conclusion").  For a candidate
+ * a learned model as future work: es page, "Significado y
+ * Reivindicaciones" / "Direcciones Futuras").  For a candidate
  * (path, split cap) the features f[0..PKV_COST_FEATURES) of its plan are
  *   f0 = 1
  *   f1 = kernel launches per step
@@ -394,6 +397,25 @@ pkv_status pkv_append_kv(const pkv_problem* prob, const void* k_new, const void*
  */
 pkv_status pkv_policy(const pkv_policy_table* table, int32_t batch, int32_t max_len,
                       int32_t* path_out, int32_t* splits_out);
+
+/*
+ * Default path choice of the engine: for B = 1 the calibrated table's rule
+ * for (1, N_1) (pkv_policy: the one row's length fixes the workload); for
+ * B >= 2 the learned cost model's choice among its candidates
+ * (pkv_policy_model), because with several rows the length mix, not only
+ * (B, N_max), decides how evenly the split launch loads the CUs.  The pages
+ * calibrate thresholds on (B, N_max) ("Metodologia / 2. Politica Adaptativa
+ * Calibrada", es page) and name a learned cost model as the next step
+ * ("Significado y Reivindicaciones" / "Direcciones Futuras"); this policy
+ * keeps the first where it sees the whole workload and takes the second
+ * elsewhere.  Host only.  scratch_host as for pkv_policy_model.
+ * Errors: PKV_EINVAL (null pointer, or as pkv_policy / pkv_policy_model),
+ * PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE (a length outside
+ * [0, max_pages_per_row * P], or no table rule matches at B = 1).
+ */
+pkv_status pkv_policy_default(const pkv_policy_table* table, const pkv_cost_model* model,
+                              const pkv_problem* prob, const int32_t* seq_lens_host,
+                              int32_t* scratch_host, int32_t* path_out, int32_t* splits_out);
 
 /* Static description of a status code; never NULL. */
 const char* pkv_status_str(pkv_status status);

@@ -21,7 +21,8 @@ what the PersistentKV summary pages define:
 * ``append_kv`` -- storing a step's new key/value through the block table
   (the input side of the decode step; not described on the pages).
 * ``cost`` -- plan features and the argmin choice of a learned per-path
-  linear cost model (future work on the pages, "Conclusion").
+  linear cost model (future work on the pages: es page,
+  "Significado y Reivindicaciones" / "Direcciones Futuras").
 """
 from .attention import (  # noqa: F401
     attention,

@@ -4,9 +4,12 @@ Parity status: pinned.  ``tests/test_oracle.py`` checks ``attention`` against
 torch's dense scaled-dot-product attention on contiguous K/V that were then
 scattered into a shuffled page pool, against closed forms (one token, constant
 keys, zero query, a hand-worked two-token example in ``tests/golden/``), and
-against invariants (page permutation, score shift, linearity in V); and it
+against invariants (page permutation, score shift, linearity in V); it
 checks ``split_state`` + ``merge`` against the unsplit result for random
-partitions.
+partitions; and it checks ``split_states_for_plan`` by merging the states of
+every task of ``oracle.plan`` (all four paths, lengths off page boundaries,
+rows shorter than the split cap, empty rows, NaN page tails) back into the
+unsplit result.
 """
 from __future__ import annotations
 

@@ -3,8 +3,9 @@ candidate (path, split cap) and the argmin choice of a per-path linear model
 of the step time.
 
 A learned cost model is what the PersistentKV summary pages leave as future
-work (section "Conclusion"; the paper's own policy, "2. Calibrated adaptive
-policy", uses hand-calibrated thresholds).  The features restate counters of
+work (es page, "Significado y Reivindicaciones" / "Direcciones Futuras";
+the paper's own policy, "2. Calibrated adaptive policy", uses
+hand-calibrated thresholds).  The features restate counters of
 ``oracle.planner.plan`` in natural units:
 
   f0 = 1, f1 = launches per step, f2 = real-KV MB, f3 = merge-state MB,
@@ -18,8 +19,9 @@ policy", uses hand-calibrated thresholds).  The features restate counters of
 The model predicts microseconds as w[path] . f; the choice is the argmin.
 
 Parity status: pinned by hand-computed features (tests/test_oracle_cost.py)
-and, through them, by the planner pins; the fitted weights are measured
-values and are not pinned.
+and, through them, by the planner pins; ``predict_us`` by hand-computed dot
+products and ``choose`` by a hand-worked argmin and a tie (the first
+candidate wins).  The fitted weights are measured values and are not pinned.
 """
 from __future__ import annotations
 

@@ -21,7 +21,10 @@ import numpy as np
 import torch  # noqa: F401  (load order matters, see above)
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
+# PKV_LIBRARY names another build of the same library (for instance the
+# sanitizer build of its host code that the CPU tests load); the default is
+# the in-tree libpkv.so.
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(PKG_DIR, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE, PKV_ENOSPC, PKV_EHIP = 0, -1, -2, -3, -4, -5, -6
 PKV_F16, PKV_BF16 = 0, 1
@@ -39,7 +42,8 @@ KERNEL_IDS = {"auto": PKV_KERNEL_AUTO, "valu": PKV_KERNEL_VALU, "mfma": PKV_KERN
 EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pkv_merge",
             "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_decode_selfplan",
             "pkv_merge_selfplan", "pkv_append_kv",
-            "pkv_policy", "pkv_cost_features", "pkv_policy_model", "pkv_status_str")
+            "pkv_policy", "pkv_cost_features", "pkv_policy_model", "pkv_policy_default",
+            "pkv_status_str")
 PKV_COST_FEATURES = 7
 
 
@@ -132,6 +136,10 @@ def _load() -> ctypes.CDLL:
     lib.pkv_policy_model.argtypes = [prob_p, ctypes.POINTER(pkv_cost_model), vp, vp,
                                      ctypes.POINTER(i32), ctypes.POINTER(i32), f32p]
     lib.pkv_policy_model.restype = i32
+    lib.pkv_policy_default.argtypes = [ctypes.POINTER(pkv_policy_table),
+                                       ctypes.POINTER(pkv_cost_model), prob_p, vp, vp,
+                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.pkv_policy_default.restype = i32
     lib.pkv_status_str.argtypes = [i32]
     lib.pkv_status_str.restype = ctypes.c_char_p
     return lib
@@ -319,6 +327,28 @@ def pkv_policy_model(prob: pkv_problem, candidates, weights, num_cus: int, seq_l
         ctypes.byref(prob), ctypes.byref(model), lens.ctypes.data, scratch.ctypes.data,
         ctypes.byref(path), ctypes.byref(splits), ctypes.byref(pred)))
     return path.value, splits.value, pred.value
+
+
+def pkv_policy_default(rules, prob: pkv_problem, candidates, weights, num_cus: int,
+                       seq_lens_host):
+    """rules as for pkv_policy; candidates / weights / num_cus as for
+    pkv_policy_model.  Returns (path_id, splits)."""
+    flat = np.ascontiguousarray(np.asarray(rules, dtype=np.int32).reshape(-1))
+    table = pkv_policy_table(len(flat) // 6,
+                             flat.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    cand = np.ascontiguousarray(np.asarray(candidates, dtype=np.int32).reshape(-1))
+    w = np.ascontiguousarray(np.asarray(weights, dtype=np.float32).reshape(-1))
+    if w.size != 4 * PKV_COST_FEATURES:
+        raise ValueError("weights must be [4][PKV_COST_FEATURES]")
+    model = pkv_cost_model(len(cand) // 2, cand.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                           w.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), num_cus)
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    scratch = np.empty(max(1, prob.batch), dtype=np.int32)
+    path, splits = ctypes.c_int32(), ctypes.c_int32()
+    _check("pkv_policy_default", LIB.pkv_policy_default(
+        ctypes.byref(table), ctypes.byref(model), ctypes.byref(prob), lens.ctypes.data,
+        scratch.ctypes.data, ctypes.byref(path), ctypes.byref(splits)))
+    return path.value, splits.value
 
 
 def decode_plan(plan_host) -> dict:

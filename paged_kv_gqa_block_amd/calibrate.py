@@ -110,6 +110,91 @@ def build_rules(calib: dict):
     return rules
 
 
+TRACE_CELLS = ("long", "bimodal", "zipf", "uniform", "tiny")
+HELDOUT_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "policy_heldout.json")
+MIN_BAND = 0.005  # floor of a cell's noise band (0.5 %)
+
+
+def rel_iqr(xs) -> float:
+    """Interquartile range over the median: the run-to-run spread of one
+    configuration's repeats."""
+    q1, q2, q3 = np.percentile(np.asarray(xs, dtype=np.float64), [25, 50, 75])
+    return float((q3 - q1) / q2) if q2 > 0 else 0.0
+
+
+def check_default(out_path: str, steps: int, warmup: int, repeats: int) -> bool:
+    """Held-out check of the engine's default policy (pkv_policy_default).
+
+    Cells: both sweep families at every batch size and the trace workloads,
+    all on the held-out seed.  In each cell the default policy's choice and
+    the four fixed single paths are timed with interleaved repeats.  The
+    cell's noise band is the larger relative interquartile range of the
+    policy's and the best single path's repeats (at least MIN_BAND): the
+    policy passes the cell when its median is at most the best single
+    path's median times (1 + band).  Over all cells its summed time must
+    also not exceed any single path's sum.
+    """
+    rules = engine.load_policy_table()
+    model = engine.load_cost_model()
+    cells = [(pattern.format(b), family) for family, pattern in FAMILIES
+             for b in traces.POLICY_BATCHES] + [(t, "trace") for t in TRACE_CELLS]
+    record, ok_all = {}, True
+    # Single paths at the workload's own split cap (32, or 4 for the tiny
+    # workload), summed per path.
+    total_policy, total_single = 0.0, {p: 0.0 for p, _ in SINGLE_PATHS}
+    for name, family in cells:
+        spec = traces.get_spec(name)
+        w = traces.generate(spec, traces.HELD_OUT_SEED)
+        lens = w["seq_lens"].numpy()
+        path, s = engine.choose_default(rules, model, engine.problem_from_workload(w), lens)
+        singles = [(p, spec.splits if p != "nosplit" else 1) for p, _ in SINGLE_PATHS]
+        configs = list(dict.fromkeys(singles + [(path, s)]))
+        wd = engine.to_device(w)
+        engine.validate_inputs(wd)
+        views = timing.pool_copies(wd, 1.0, max_copies=8)
+        med, runs = timing.time_paths_interleaved(w, views, configs, "auto", steps, warmup,
+                                                  repeats=repeats, return_runs=True)
+        del views, wd
+        torch.cuda.empty_cache()
+        key = f"{path}:{s}"
+        best_key = min((f"{p}:{ss}" for p, ss in singles), key=lambda k: med[k])
+        band = max(MIN_BAND, rel_iqr(runs[key]), rel_iqr(runs[best_key]))
+        ratio = med[key] / med[best_key]
+        ok = ratio <= 1 + band
+        ok_all &= ok
+        total_policy += med[key]
+        for p, ss in singles:
+            total_single[p] += med[f"{p}:{ss}"]
+        record[name] = {"family": family, "batch": spec.batch, "n_max": int(lens.max()),
+                        "policy": key, "best_single": best_key,
+                        "times_us": {k: round(v, 2) for k, v in med.items()},
+                        "spread": {k: round(rel_iqr(v), 4) for k, v in runs.items()},
+                        "band": round(band, 4), "policy_over_best_single": round(ratio, 4),
+                        "ok": ok}
+        log(f"  default policy {name}: {key} {med[key]:.2f} us, best single {best_key} "
+            f"{med[best_key]:.2f} us, ratio {ratio:.4f} band {band:.4f} -> "
+            f"{'ok' if ok else 'SLOWER'}")
+    sums_ok = all(total_policy <= v for v in total_single.values())
+    doc = {
+        "about": "Held-out check of the default policy (pkv_policy_default: calibrated table "
+                 "for B = 1, learned cost model over workqueue and no-split candidates for "
+                 "B >= 2) against the four fixed single paths.",
+        "heldout_seed": traces.HELD_OUT_SEED,
+        "device": torch.cuda.get_device_name(0),
+        "steps_per_repeat": steps, "repeats": repeats, "min_band": MIN_BAND,
+        "cells": record,
+        "total_us": {"policy": round(total_policy, 2),
+                     **{k: round(v, 2) for k, v in total_single.items()}},
+        "sums_ok": sums_ok,
+        "all_cells_ok": ok_all,
+    }
+    with open(out_path, "w") as f:
+        json.dump(doc, f, indent=1)
+    log(f"wrote {out_path}: cells {'all ok' if ok_all else 'NOT all ok'}, sums "
+        f"{'ok' if sums_ok else 'NOT ok'}; totals {doc['total_us']}")
+    return ok_all and sums_ok
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--out", default=engine.POLICY_TABLE_PATH)
@@ -118,8 +203,15 @@ def main(argv=None):
     ap.add_argument("--rules-from", default=None,
                     help="reuse the calibration timings of this table; rebuild the rules "
                          "and rerun only the held-out check")
+    ap.add_argument("--check-default", action="store_true",
+                    help="only run the held-out check of the default policy (table for "
+                         "B = 1, cost model for B >= 2) and write policy_heldout.json")
+    ap.add_argument("--repeats", type=int, default=11)
     args = ap.parse_args(argv)
     assert torch.cuda.is_available(), "calibration needs a GPU"
+    if args.check_default:
+        out = args.out if args.out != engine.POLICY_TABLE_PATH else HELDOUT_PATH
+        return 0 if check_default(out, args.steps, args.warmup, args.repeats) else 1
     t0 = time.time()
     calib, held = {}, {}
     if args.rules_from:

@@ -11,7 +11,8 @@
                                                       #      choices on stored timings
 
 The PersistentKV summary pages leave a learned cost model as future work
-("Conclusion").  Here the model is, for each split kernel (matrix-core or
+("Significado y Reivindicaciones" /
+"Direcciones Futuras" on the es page).  Here the model is, for each split kernel (matrix-core or
 vector-ALU) and each path, one linear function of the plan features of
 include/pkv.h (pkv_cost_features: launches, KV and state megabytes, per-CU
 critical pages, grid items, tasks), predicting the step time in

@@ -59,7 +59,8 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
   const int32_t* w = nullptr;
   st = check_plan(prob, plan_host, &w);
   if (st != PKV_OK) return st;
-  if (!plan_dev || !q || !k_pool || !v_pool || !block_table || !seq_lens_dev) return PKV_EINVAL;
+  (void)seq_lens_dev;  // every path takes the row lengths from the plan
+  if (!plan_dev || !q || !k_pool || !v_pool || !block_table) return PKV_EINVAL;
   st = check_kernel_shape(prob);
   if (st != PKV_OK) return st;
   const int path = w[kPath];
@@ -74,7 +75,6 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.block_table = block_table;
-  a.seq_lens = seq_lens_dev;
   a.st_m = st_m;
   a.st_l = st_l;
   a.st_o = st_o;
@@ -86,6 +86,10 @@ extern "C" pkv_status pkv_decode(const pkv_problem* prob, const void* plan_host,
   a.splits = w[kSplits];
   a.scale_log2 = prob->sm_scale * kLog2e;
   const int32_t* dev = static_cast<const int32_t*>(plan_dev);
+  // The no-split kernel reads each row's length from the plan's row_len
+  // array: the lengths pkv_plan validated, the same ones every other path
+  // uses.
+  a.seq_lens = dev + PKV_PLAN_HEADER_WORDS;
 
   if (path == PKV_WORKQUEUE) {
     const int n = w[kNumTasks];
@@ -377,6 +381,8 @@ extern "C" pkv_status pkv_append_kv(const pkv_problem* prob, const void* k_new,
   if (st != PKV_OK) return st;
   if (!k_new || !v_new || !block_table || !positions_dev || !k_pool || !v_pool)
     return PKV_EINVAL;
+  // One workgroup per (row, KV head).
+  if (int64_t(prob->batch) * prob->num_kv_heads > kMaxGridGroups) return PKV_ERANGE;
   AppendArgs a{};
   a.k_new = k_new;
   a.v_new = v_new;

@@ -1,9 +1,10 @@
 // Learned cost model for the path choice: plan features of a candidate
 // (path, split cap) in natural units and a per-path linear model of the step
 // time, fitted to measured step times.  The PersistentKV summary pages leave
-// such a model as future work ("Conclusion"; "2. Calibrated adaptive policy"
-// uses hand-calibrated thresholds instead).  Host code only; it allocates
-// nothing (bucket orders use the caller's scratch, per-CU sums the stack).
+// such a model as future work ("Significado y Reivindicaciones" / "Direcciones
+// Futuras", es page; "2. Calibrated adaptive policy" uses hand-calibrated
+// thresholds instead).  Host code only; it allocates nothing (bucket orders
+// use the caller's scratch, per-CU sums the stack).
 #include <algorithm>
 #include <cstdint>
 #include <cmath>
@@ -188,4 +189,25 @@ extern "C" pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_m
   *splits_out = model->candidates[2 * best_k + 1];
   if (predicted_us_out) *predicted_us_out = float(best);
   return PKV_OK;
+}
+
+extern "C" pkv_status pkv_policy_default(const pkv_policy_table* table,
+                                         const pkv_cost_model* model, const pkv_problem* prob,
+                                         const int32_t* seq_lens_host, int32_t* scratch_host,
+                                         int32_t* path_out, int32_t* splits_out) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  if (!table || !model || !seq_lens_host || !path_out || !splits_out) return PKV_EINVAL;
+  const int64_t cap = int64_t(prob->max_pages_per_row) * prob->page_size;
+  int32_t n_max = 0;
+  for (int32_t i = 0; i < prob->batch; ++i) {
+    if (seq_lens_host[i] < 0 || seq_lens_host[i] > cap) return PKV_ERANGE;
+    n_max = std::max(n_max, seq_lens_host[i]);
+  }
+  // One row: its length is N_max, so the (B, N_max) table sees the whole
+  // workload.  Several rows: the length mix decides the load balance, which
+  // the model's per-CU feature sees and the table's key does not.
+  if (prob->batch == 1) return pkv_policy(table, 1, n_max, path_out, splits_out);
+  return pkv_policy_model(prob, model, seq_lens_host, scratch_host, path_out, splits_out,
+                          nullptr);
 }

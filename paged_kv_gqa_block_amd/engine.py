@@ -205,6 +205,24 @@ def choose_model(model, prob: _lib.pkv_problem, seq_lens_host):
     return PATH_NAMES[path], splits, pred
 
 
+# Candidates of the default policy's cost-model leg (B >= 2): the compact
+# workqueue at each split cap, and the single-pass kernel.  On the calibration
+# and held-out draws of every sweep and trace workload the full candidate list
+# picks the same (path, split cap) at B >= 2, at a third of the host time.
+DEFAULT_MODEL_PATHS = (PKV_WORKQUEUE, PKV_NOSPLIT)
+
+
+def choose_default(rules, model, prob: _lib.pkv_problem, seq_lens_host):
+    """Path name and split cap of the engine's default policy
+    (pkv_policy_default): the calibrated table for one row, the learned cost
+    model (workqueue and no-split candidates) for several."""
+    cands, weights, num_cus = model
+    cands = [c for c in cands if c[0] in DEFAULT_MODEL_PATHS]
+    path, splits = _lib.pkv_policy_default(rules, prob, cands, weights[split_kernel_of(prob)],
+                                           num_cus, seq_lens_host)
+    return PATH_NAMES[path], splits
+
+
 def validate_inputs(w: dict) -> None:
     """Host-side checks that the tensors match what the kernels assume.
 

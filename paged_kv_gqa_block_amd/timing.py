@@ -16,13 +16,23 @@ import time
 import numpy as np
 import torch
 
-from . import engine
+from . import _lib, engine
+
+
+# MI355X's Infinity Cache (MALL) holds 256 MiB; the rotated copies always
+# total at least twice that, so no step reads K/V that a recent step left there.
+MALL_BYTES = 256 << 20
 
 
 def pool_copies(wd: dict, copies_gib: float, max_copies: int = 64):
-    """Views of the workload on n copies of the pools (n * pool size >= copies_gib)."""
+    """Views of the workload on n copies of the pools: n * pool size >=
+    copies_gib, at most max_copies copies unless fewer would total less than
+    2 x the 256 MiB Infinity Cache (small pools then get as many copies as
+    that takes)."""
     pool_bytes = wd["k_pool"].numel() * wd["k_pool"].element_size() * 2
-    n = max(1, min(max_copies, math.ceil(copies_gib * (1 << 30) / pool_bytes)))
+    want = math.ceil(copies_gib * (1 << 30) / pool_bytes)
+    floor = math.ceil(2 * MALL_BYTES / pool_bytes)
+    n = max(1, floor, min(max_copies, want))
     views = [wd]
     for _ in range(n - 1):
         views.append(dict(wd, k_pool=wd["k_pool"].clone(), v_pool=wd["v_pool"].clone()))
@@ -117,13 +127,14 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
 
 
 def time_paths_interleaved(w: dict, views, configs, kernel: str = "auto", steps: int = 30,
-                           warmup: int = 5, repeats: int = 7) -> dict:
+                           warmup: int = 5, repeats: int = 7, return_runs: bool = False):
     """Step time of several (path, split cap) configurations of one workload.
 
     The timed loops alternate between the configurations (repeat r of every
     configuration before repeat r + 1 of any), so a drift of the GPU's clock
     during the measurement moves all of them alike; each result is the median
-    over its repeats.  Returns {"path:splits": step_us}.
+    over its repeats.  Returns {"path:splits": step_us}, and with
+    ``return_runs`` also {"path:splits": [µs of each repeat]}.
     """
     prob = engine.problem_from_workload(w, kernel)
     stream = torch.cuda.current_stream()
@@ -148,7 +159,8 @@ def time_paths_interleaved(w: dict, views, configs, kernel: str = "auto", steps:
             torch.cuda.synchronize()
             runs[key].append(1e3 * e0.elapsed_time(e1) / steps)
             k0 += steps
-    return {k: statistics.median(v) for k, v in runs.items()}
+    med = {k: statistics.median(v) for k, v in runs.items()}
+    return (med, runs) if return_runs else med
 
 
 def time_read_probe(w: dict, views, path: str, splits: int, steps: int = 50,
@@ -231,9 +243,11 @@ def time_device_path(w: dict, views, splits: int, steps: int = 50, warmup: int =
             one(i)
             torch.cuda.synchronize()
             sync_us.append((time.perf_counter() - t) * 1e6)
-    pages = (w["seq_lens"].numpy().astype(np.int64) + 15) // 16
-    pps = max(1, -(-int(pages.max(initial=0)) // splits))
-    n_tasks = int(prob.num_kv_heads * (-(-pages // pps)).sum())
+    # Task count of the same workqueue, from the library's host planner (host
+    # plan only, no device copy).
+    lens = np.ascontiguousarray(w["seq_lens"].numpy(), dtype=np.int32)
+    plan_host = np.zeros(_lib.pkv_plan_bytes(prob, _lib.PKV_WORKQUEUE, splits) // 4, np.int32)
+    n_tasks = int(_lib.pkv_plan(prob, lens, _lib.PKV_WORKQUEUE, splits, plan_host).n_tasks)
     return {
         "path": ("workqueue_selfplan" if selfplan else "workqueue_device") +
                 ("_graph" if graph else ""),

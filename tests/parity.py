@@ -4,9 +4,16 @@ Tolerances (reading of "FP16 tolerance", which the pages give without a
 number; the bound is max-abs <= 2e-3 and relative L2 <= 1e-3):
 * fp16 output vs the raw fp64 oracle.
 * bf16 output vs the fp64 oracle rounded to bf16 (nearest-even), because the
-  output rounding alone already exceeds 1e-3 relative L2 for bf16.  An
-  element may also differ by one bf16 unit in the last place, which happens
-  when the fp32 kernel result and the fp64 value straddle a rounding midpoint.
+  output rounding alone already exceeds 1e-3 relative L2 for bf16.  Where the
+  difference exceeds 2e-3 (bf16 outputs of magnitude >= 0.5, whose unit in
+  the last place is larger than that), the element must be the neighbouring
+  bf16 value on the fp64 value's side, and the fp64 value must lie within
+  BF16_MIDPOINT_REL (relative) of the midpoint between the two: the kernel's
+  fp32 result can only round the other way there.  At most
+  BF16_FLIP_FRACTION of the elements may be such flips.
+  BF16_MIDPOINT_REL bounds the kernel's relative error in fp32: P enters the
+  P*V product as two bf16 parts carrying 16 significant bits (relative error
+  <= 2^-17 = 7.6e-6 per term), plus fp32 accumulation and the normalisation.
 * lse (natural log) within 2e-4 absolute.
 * partial states: lse_s = m + ln l within 2e-4, o/l within 1e-4 (max-abs).
 """
@@ -23,6 +30,8 @@ from paged_kv_gqa_block_amd import traces
 MAX_ABS = 2e-3
 REL_L2 = 1e-3
 LSE_ABS = 2e-4
+BF16_MIDPOINT_REL = 2e-5
+BF16_FLIP_FRACTION = 1e-3
 
 
 def say(*args):
@@ -42,6 +51,15 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.where(ax > 0, 2.0 ** (e - 7), 2.0 ** -133)
 
 
+def bf16_midpoint_flips(g: np.ndarray, r: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Elements where g is the bf16 neighbour of r = bf16(ref) on ref's side and
+    ref lies within BF16_MIDPOINT_REL (relative) of the midpoint of g and r."""
+    neighbour = np.abs(g - r) <= bf16_ulp(r) * 1.0001
+    same_side = np.sign(g - r) == np.sign(ref - r)
+    near_mid = np.abs(ref - 0.5 * (g + r)) <= BF16_MIDPOINT_REL * np.abs(ref)
+    return neighbour & same_side & (g != r) & near_mid
+
+
 def check_out(got: torch.Tensor, ref: np.ndarray, dtype: str, rows=None, label=""):
     g = got.detach().float().cpu().numpy().astype(np.float64)
     if rows is not None:
@@ -50,10 +68,16 @@ def check_out(got: torch.Tensor, ref: np.ndarray, dtype: str, rows=None, label="
     if dtype == "bf16":
         r = oracle.round_to_bf16(ref)
         diff = np.abs(g - r)
-        allowed = np.maximum(MAX_ABS, bf16_ulp(r) * 1.0001)
-        bad = diff > allowed
-        assert not bad.any(), f"{label}: {bad.sum()} elements beyond max(2e-3, 1 ulp); " \
-                              f"worst {diff.max():.3e}"
+        over = diff > MAX_ABS
+        if over.any():
+            flips = bf16_midpoint_flips(g, r, ref)
+            bad = over & ~flips
+            assert not bad.any(), (
+                f"{label}: {bad.sum()} elements beyond 2e-3 that are not a rounding flip at a "
+                f"midpoint; worst {diff[bad].max():.3e}")
+            n_flip = int(over.sum())
+            assert n_flip <= max(1, BF16_FLIP_FRACTION * g.size), \
+                f"{label}: {n_flip} midpoint flips of {g.size} elements"
     else:
         r = ref
         diff = np.abs(g - r)

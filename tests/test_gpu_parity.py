@@ -352,3 +352,103 @@ def test_random_equal_split_counts_every_split_path(seed):
             step, _ = _run(w, path, splits, kernel)
             check_out(step.out, ref_out, dtype, label=f"equal{seed}/{kernel}/{path}")
             check_lse(step.lse, ref_lse, label=f"equal{seed}/{kernel}/{path}")
+
+
+def _peaked(w, q_scale, targets):
+    """Sharply peaked scores.  q is multiplied by q_scale (a typical score then
+    has standard deviation q_scale), and for every row and KV head g the key of
+    a few planted tokens is set so that the score of query head g * G is
+    targets[k] (up to the 16-bit rounding of the key): the planted tokens lie in
+    different splits, the largest one late in its split (its page raises the
+    running maximum by a wide margin), and the other splits' maxima sit tens of
+    natural-log units below the row maximum (their weights underflow)."""
+    spec = w["spec"]
+    dt = w["q"].dtype
+    q = (w["q"].float() * q_scale).to(dt)
+    k_pool = w["k_pool"].clone()
+    bt = w["block_table"].numpy()
+    grp = spec.group
+    for i, n in enumerate(w["seq_lens"].numpy()):
+        n = int(n)
+        if n == 0:
+            continue
+        spots = [min(n - 1, int(f * n)) for f in (0.62, 0.15, 0.97)][:len(targets)]
+        for k, (t, target) in enumerate(zip(spots, targets)):
+            page, slot = int(bt[i, t // spec.page_size]), t % spec.page_size
+            for g in range(spec.num_kv_heads):
+                qh = q[i, g * grp].double()
+                key = qh * (target / w["scale"] / float(qh @ qh))
+                k_pool[page, g, slot] = key.to(dt)
+    return dict(w, q=q, k_pool=k_pool)
+
+
+@pytest.mark.parametrize("dtype", ("f16", "bf16"))
+@pytest.mark.parametrize("regime,q_scale,targets", [
+    ("spread", 12.0, (60.0, 58.0, 55.0)),    # P spans fp16's subnormal range
+    ("extreme", 4.0, (200.0, 199.0, 120.0)),  # every other split underflows
+])
+def test_peaked_softmax_every_path(regime, q_scale, targets, dtype):
+    """Scores spanning about +-50 to +-200 natural-log units: one or a few
+    tokens in different splits dominate, the merge weights of the other splits
+    underflow, the running maximum grows by a wide margin inside a split, and
+    in the spread regime the P values of a split reach fp16's subnormal range.
+    Every path and both kernels, fp16 and bf16, against the oracle."""
+    lens = np.array([32768, 5000, 777, 0], dtype=np.int32)
+    spec = traces.custom_spec(4, 32, 8, 128, splits=32, dtype=dtype)
+    w = _peaked(traces.generate(spec, SEED, seq_lens=lens), q_scale, targets)
+    say(f"[peaked {regime}] {dtype} q_scale={q_scale} targets={targets}")
+    ref_out, ref_lse = oracle_out(w)
+    assert np.abs(ref_out).max() > 0.5  # outputs dominated by a few V rows
+    for kernel in KERNELS:
+        for path, s in (("workqueue", 32), ("bucketed", 32), ("padded", 32), ("nosplit", 1),
+                        ("workqueue", 7)):
+            step, _ = _run(w, path, s, kernel)
+            check_out(step.out, ref_out, dtype, label=f"peaked/{regime}/{kernel}/{path}:{s}")
+            check_lse(step.lse, ref_lse, label=f"peaked/{regime}/{kernel}/{path}:{s}")
+
+
+@pytest.mark.parametrize("name", ("long", "bimodal", "zipf", "uniform", "tiny", "policy_b1",
+                                  "policy_b8", "policy_short_b4", "policy_short_b16",
+                                  "policy_b32"))
+def test_cost_model_choice_matches_oracle(name):
+    """The learned cost model's choice (pkv_policy_model with the weights of
+    the problem's split kernel) run through the C ABI on the trace and sweep
+    workloads, against the oracle (B = 32 on sampled rows)."""
+    w = traces.generate(traces.get_spec(name), SEED)
+    spec = w["spec"]
+    lens = w["seq_lens"].numpy()
+    path, s, pred = engine.choose_model(engine.load_cost_model(),
+                                        engine.problem_from_workload(w), lens)
+    rows = None if spec.batch <= 16 else sorted({0, spec.batch // 2, int(lens.argmax()),
+                                                 spec.batch - 1})
+    say(f"[cost model {name}] choice {path}:{s} predicted {pred:.1f} us rows={rows}")
+    ref_out, ref_lse = oracle_out(w, rows=rows)
+    step, _ = _run(w, path, s, "auto")
+    check_out(step.out, ref_out, spec.dtype, rows=rows, label=f"model/{name}/{path}:{s}")
+    check_lse(step.lse, ref_lse, rows=rows, label=f"model/{name}/{path}:{s}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_nosplit_takes_row_lengths_from_the_plan(kernel):
+    """pkv_decode reads every row's length from the plan on every path: on the
+    no-split path a device length array that disagrees with the plan (here
+    each entry within the row's table capacity, so any read stays in bounds)
+    changes nothing; the output matches the oracle at the planned lengths."""
+    from paged_kv_gqa_block_amd import _lib
+
+    d = 128 if kernel == "mfma" else 64
+    lens = np.array([300, 17, 0], dtype=np.int32)
+    spec = traces.custom_spec(3, 8, 2, d, splits=4)
+    w = traces.generate(spec, SEED, seq_lens=lens)
+    say(f"[nosplit plan lengths] kernel={kernel}")
+    wd = engine.to_device(w)
+    engine.validate_inputs(wd)
+    step = engine.DecodeStep(engine.problem_from_workload(w, kernel), "nosplit", 1)
+    step.plan(wd["seq_lens_host"])
+    stale = torch.tensor([17, 300, 250], dtype=torch.int32, device="cuda")
+    _lib.pkv_decode(step.prob, step.plan_host, step.plan_dev, wd["q"], wd["k_pool"],
+                    wd["v_pool"], wd["block_table"], stale, None, None, None, step.out, step.lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_out(w)
+    check_out(step.out, ref_out, "f16", label="nosplit/plan lengths")
+    check_lse(step.lse, ref_lse, label="nosplit/plan lengths")

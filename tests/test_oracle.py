@@ -315,3 +315,41 @@ def test_append_one_by_one_rebuilds_the_dense_sequence():
     got_k, got_v = oracle.gather_row(k, v, bt[0], n, 1, p, "f16")
     np.testing.assert_array_equal(got_k, kd[:, 1].astype(np.float64))
     np.testing.assert_array_equal(got_v, vd[:, 1].astype(np.float64))
+
+
+@pytest.mark.parametrize("path", ["workqueue", "bucketed", "padded", "nosplit"])
+@pytest.mark.parametrize("seed", range(4))
+def test_plan_task_states_merge_to_unsplit_attention(path, seed):
+    """oracle.split_states_for_plan over every task of oracle.plan, merged per
+    (row, KV head), equals oracle.attention: the tasks cover each row's real
+    tokens exactly once (lengths off page boundaries, rows shorter than the
+    split cap, an empty row), and each task reads only its own token range
+    (page tails hold NaN)."""
+    rng = np.random.default_rng(4100 + seed)
+    page = int(rng.choice([4, 16]))
+    lens = [int(x) for x in rng.choice([0, 1, page - 1, page, page + 1, 3 * page + 2, 57, 200],
+                                       size=5)]
+    lens[int(rng.integers(0, 5))] = 0
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 3, 4]))
+    splits = int(rng.choice([1, 3, 8, 64]))
+    d = 16
+    q, _, _, k_pool, v_pool, bt = _random_case(rng, len(lens), hq, hkv, d, lens, page)
+    scale = 1.0 / math.sqrt(d)
+    ref, ref_lse = attention(q, k_pool, v_pool, bt, np.array(lens), scale, page, "f16")
+    p = oracle.plan(lens, hkv, hq, d, page, splits, path)
+    grp = hq // hkv
+    m, l, o = oracle.split_states_for_plan(q, k_pool, v_pool, bt, p.tasks, scale, page, "f16",
+                                           grp, lens)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    for i, n in enumerate(lens):
+        for g in range(hkv):
+            idx = [j for j, t in enumerate(p.tasks) if t[0] == i and t[1] == g]
+            if n == 0:
+                assert not idx
+                continue
+            out, lse = merge(m[idx], l[idx], o[idx])
+            np.testing.assert_allclose(out, ref[i, g * grp:(g + 1) * grp], rtol=1e-12,
+                                       atol=1e-12)
+            np.testing.assert_allclose(lse, ref_lse[i, g * grp:(g + 1) * grp], rtol=1e-12,
+                                       atol=1e-12)

@@ -113,3 +113,102 @@ def test_policy_model_errors():
     with pytest.raises(PkvError) as e:
         _lib.pkv_cost_features(prob, [10, 20], 4, 8, 256)
     assert e.value.status == _lib.PKV_EINVAL
+
+
+# Hand-picked weights (rows: bucketed, workqueue, nosplit, padded) whose
+# predictions on the HAND features above are worked out by hand:
+#   bucketed  0 + 1 * 6 (launches) + 1 * 22 (critical pages)          = 28
+#   workqueue 10 + 2 * 2 (launches) + 0.5 * 22 (critical pages)       = 25
+#   nosplit   1 * 38 (critical pages)                                 = 38
+#   padded    1 + 100 * 0.032 (grid items / 1000)                     = 4.2
+HAND_W = [[0, 1, 0, 0, 1, 0, 0],
+          [10, 2, 0, 0, 0.5, 0, 0],
+          [0, 0, 0, 0, 1, 0, 0],
+          [1, 0, 0, 0, 0, 100, 0]]
+HAND_Y = {"bucketed": 28.0, "workqueue": 25.0, "nosplit": 38.0, "padded": 4.2}
+HAND_CANDS = [("workqueue", 4), ("bucketed", 4), ("nosplit", 1), ("padded", 4)]
+
+
+@pytest.mark.parametrize("path", sorted(HAND))
+def test_predict_us_is_the_hand_computed_dot_product(path):
+    assert abs(cost.predict_us(HAND_W, path, HAND[path]) - HAND_Y[path]) <= 1e-12
+
+
+def test_choice_is_the_hand_worked_argmin():
+    path, s, y = cost.choose(HAND_W, HAND_CANDS, LENS, 2, 4, 64, 16, 4)
+    assert (path, s) == ("padded", 4) and abs(y - 4.2) <= 1e-12
+    # The C entry point makes the same choice.
+    prob = _lib.make_problem(4, 4, 2, 64, 16, 4096, 64)
+    cands = [(_lib.PATH_IDS[p], ss) for p, ss in HAND_CANDS]
+    w = np.asarray(HAND_W, dtype=np.float32)
+    cp, cs, cy = _lib.pkv_policy_model(prob, cands, w, 4, LENS)
+    assert (PATH_NAMES[cp], cs) == ("padded", 4) and abs(cy - 4.2) <= 1e-5
+
+
+def test_choice_tie_goes_to_the_first_candidate():
+    # bucketed now predicts 3 + 22 = 25, the workqueue's value; padded 100 + 3.2.
+    w = [list(r) for r in HAND_W]
+    w[0] = [3, 0, 0, 0, 1, 0, 0]
+    w[3] = [100, 0, 0, 0, 0, 100, 0]
+    assert cost.choose(w, HAND_CANDS, LENS, 2, 4, 64, 16, 4)[:2] == ("workqueue", 4)
+    swapped = [HAND_CANDS[1], HAND_CANDS[0]] + HAND_CANDS[2:]
+    assert cost.choose(w, swapped, LENS, 2, 4, 64, 16, 4)[:2] == ("bucketed", 4)
+    prob = _lib.make_problem(4, 4, 2, 64, 16, 4096, 64)
+    wf = np.asarray(w, dtype=np.float32)
+    for order, want in ((HAND_CANDS, "workqueue"), (swapped, "bucketed")):
+        cands = [(_lib.PATH_IDS[p], ss) for p, ss in order]
+        assert PATH_NAMES[_lib.pkv_policy_model(prob, cands, wf, 4, LENS)[0]] == want
+
+
+def test_default_policy_hand_worked():
+    """One row: the table's rule for (1, N_1), whatever the model says; several
+    rows: the model's argmin, whatever the table says."""
+    from oracle import policy
+
+    rules = [(1, 1, 0, 100, "nosplit", 1), (1, 1, 101, 1 << 30, "bucketed", 16),
+             (2, 1 << 30, 0, 1 << 30, "nosplit", 1)]
+    # One row of 300 tokens: rule 2 (bucketed, 16), although the model would
+    # pick padded (HAND_W) for any lengths.
+    assert policy.choose_default(rules, HAND_W, HAND_CANDS, [300], 2, 4, 64, 16, 4) == \
+        ("bucketed", 16)
+    # LENS (four rows): the model's hand-worked argmin, padded S=4, although
+    # the table says nosplit for B >= 2.
+    assert policy.choose_default(rules, HAND_W, HAND_CANDS, LENS, 2, 4, 64, 16, 4) == \
+        ("padded", 4)
+    # The C entry point agrees on both.
+    cands = [(_lib.PATH_IDS[p], s) for p, s in HAND_CANDS]
+    w = np.asarray(HAND_W, dtype=np.float32)
+    crules = [r[:4] + (_lib.PATH_IDS[r[4]], r[5]) for r in rules]
+    one = _lib.make_problem(1, 4, 2, 64, 16, 4096, 64)
+    four = _lib.make_problem(4, 4, 2, 64, 16, 4096, 64)
+    assert _lib.pkv_policy_default(crules, one, cands, w, 4, [300]) == (_lib.PKV_BUCKETED, 16)
+    assert _lib.pkv_policy_default(crules, four, cands, w, 4, LENS) == (_lib.PKV_PADDED, 4)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_c_default_policy_matches_oracle(seed):
+    from oracle import policy
+    from paged_kv_gqa_block_amd import engine
+
+    rng = np.random.default_rng(1300 + seed)
+    rules = engine.load_policy_table()
+    cands_all, weights, cus = engine.load_cost_model()
+    cands = [c for c in cands_all if c[0] in engine.DEFAULT_MODEL_PATHS]
+    for _ in range(10):
+        b = int(rng.choice([1, 1, 2, 5, 8, 33]))
+        lens = rng.integers(0, 32768, size=b, endpoint=True)
+        lens[0] = max(1, lens[0])
+        prob = _lib.make_problem(b, 64, 8, 128, 16, 1 << 20, 2048, "bf16")
+        w = weights[engine.split_kernel_of(prob)]
+        got = _lib.pkv_policy_default(rules, prob, cands, w, cus, lens)
+        orules = [r[:4] + (PATH_NAMES[r[4]], r[5]) for r in rules]
+        ocands = [(PATH_NAMES[p], s) for p, s in cands]
+        want = policy.choose_default(orules, w.astype(np.float64), ocands, lens, 8, 64, 128, 16,
+                                     cus)
+        if b == 1:
+            assert (PATH_NAMES[got[0]], got[1]) == want
+        else:  # the model's argmin; float32 (C) and float64 (oracle) may split a near tie
+            ys = {c: cost.predict_us(w, c[0], cost.features(lens, 8, 64, 128, 16, c[1], c[0],
+                                                            cus)) for c in ocands}
+            best = min(ys.values())
+            assert ys[(PATH_NAMES[got[0]], got[1])] <= best + 1e-4 * max(1.0, abs(best))
