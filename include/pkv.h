@@ -417,6 +417,36 @@ pkv_status pkv_policy_default(const pkv_policy_table* table, const pkv_cost_mode
                               const pkv_problem* prob, const int32_t* seq_lens_host,
                               int32_t* scratch_host, int32_t* path_out, int32_t* splits_out);
 
+/*
+ * Decode step that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It is pkv_decode_selfplan followed by
+ * pkv_merge_selfplan (the same self-planned workqueue, the same two kernels,
+ * results bit-identical to that pair) with two differences:
+ *   - the partial states live in a device array owned by the library,
+ *     PKV_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ *     until the process ends; pkv_noalloc_bytes(prob, max_splits) states how
+ *     much of it a call needs (B * Hkv * max_splits slots of G * (d + 2)
+ *     floats), and a call needing more fails with PKV_ENOSPC;
+ *   - the split launch has one workgroup per possible task (B * Hkv *
+ *     max_splits, at most 2^24 - 1, else PKV_ERANGE), so no claim counter is
+ *     used and nothing in the array has to start at zero.
+ * The caller passes the inputs (as pkv_decode_selfplan) and the outputs out
+ * [B][Hq][d] and lse [B][Hq] (lse may be NULL).  Every call on one GPU uses
+ * that GPU's one array, which keeps the last call's contents: calls that
+ * overlap on one GPU (on different streams, or from different threads
+ * without ordering) race.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress) with that device current; no call
+ * allocates.  Errors: as pkv_decode_selfplan, plus PKV_ENOSPC.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+size_t pkv_noalloc_bytes(const pkv_problem* prob, int32_t max_splits);
+pkv_status pkv_attend_noalloc(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                              int32_t max_splits, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table, void* out,
+                              float* lse, hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char* pkv_status_str(pkv_status status);
 

@@ -43,7 +43,7 @@ EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pk
             "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_decode_selfplan",
             "pkv_merge_selfplan", "pkv_append_kv",
             "pkv_policy", "pkv_cost_features", "pkv_policy_model", "pkv_policy_default",
-            "pkv_status_str")
+            "pkv_noalloc_bytes", "pkv_attend_noalloc", "pkv_status_str")
 PKV_COST_FEATURES = 7
 
 
@@ -140,6 +140,10 @@ def _load() -> ctypes.CDLL:
                                        ctypes.POINTER(pkv_cost_model), prob_p, vp, vp,
                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.pkv_policy_default.restype = i32
+    lib.pkv_noalloc_bytes.argtypes = [prob_p, i32]
+    lib.pkv_noalloc_bytes.restype = ctypes.c_size_t
+    lib.pkv_attend_noalloc.argtypes = [prob_p, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.pkv_attend_noalloc.restype = i32
     lib.pkv_status_str.argtypes = [i32]
     lib.pkv_status_str.restype = ctypes.c_char_p
     return lib
@@ -280,6 +284,20 @@ def pkv_merge_selfplan(prob: pkv_problem, seq_lens_dev, max_splits: int, work_co
     _check("pkv_merge_selfplan", LIB.pkv_merge_selfplan(
         ctypes.byref(prob), _ptr(seq_lens_dev), max_splits, _ptr(work_counter_dev), _ptr(st_m),
         _ptr(st_l), _ptr(st_o), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pkv_noalloc_bytes(prob: pkv_problem, max_splits: int) -> int:
+    return LIB.pkv_noalloc_bytes(ctypes.byref(prob), max_splits)
+
+
+def pkv_attend_noalloc(prob: pkv_problem, seq_lens_dev, max_splits: int, q, k_pool, v_pool,
+                       block_table, out, lse=None, stream=None) -> None:
+    _check("pkv_attend_noalloc", LIB.pkv_attend_noalloc(
+        ctypes.byref(prob), _ptr(seq_lens_dev), max_splits, _ptr(q), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def pkv_append_kv(prob: pkv_problem, k_new, v_new, block_table, positions_dev, k_pool, v_pool,

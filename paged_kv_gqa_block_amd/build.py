@@ -24,7 +24,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [
     "planner.cpp", "api.cpp", "merge.hip", "split_valu.hip", "split_mfma.hip", "planner_device.hip",
-    "append.hip", "cost_model.cpp",
+    "append.hip", "cost_model.cpp", "noalloc.hip",
 ]
 PROBE_SOURCES = ["read_probe.hip"]
 

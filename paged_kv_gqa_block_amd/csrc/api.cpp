@@ -6,6 +6,7 @@
 
 #include "launch_limits.h"
 #include "pkv_internal.h"
+#include "selfplan_args.h"
 
 using namespace pkv;
 
@@ -292,37 +293,24 @@ extern "C" pkv_status pkv_merge_device(const pkv_problem* prob, const void* plan
 
 // ---- self-planned workqueue step --------------------------------------------
 
-namespace {
+namespace pkv {
 
-// Shared checks of the self-planned entry points.
-pkv_status check_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
-                          int32_t max_splits, const int32_t* work_counter_dev) {
+pkv_status check_selfplan_step(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                               int32_t max_splits) {
   pkv_status st = check_problem(prob);
   if (st != PKV_OK) return st;
-  if (!seq_lens_dev || !work_counter_dev) return PKV_EINVAL;
+  if (!seq_lens_dev) return PKV_EINVAL;
   if (max_splits < 1 || max_splits > 65535) return PKV_EINVAL;
   if (prob->batch > kMaxLensRows) return PKV_ERANGE;
   // Task indices and slots are 32-bit: bound the largest task count.
   if (int64_t(prob->batch) * prob->num_kv_heads * max_splits > INT32_MAX) return PKV_ERANGE;
-  return PKV_OK;
+  return check_kernel_shape(prob);
 }
 
-}  // namespace
-
-extern "C" pkv_status pkv_decode_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
-                                          int32_t max_splits, int32_t* work_counter_dev,
-                                          const void* q, const void* k_pool, const void* v_pool,
-                                          const int32_t* block_table, float* st_m, float* st_l,
-                                          float* st_o, hipStream_t stream) {
-  pkv_status st = check_selfplan(prob, seq_lens_dev, max_splits, work_counter_dev);
-  if (st != PKV_OK) return st;
-  if (!q || !k_pool || !v_pool || !block_table || !st_m || !st_l || !st_o) return PKV_EINVAL;
-  st = check_kernel_shape(prob);
-  if (st != PKV_OK) return st;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return PKV_EHIP;
+SplitArgs selfplan_split_args(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                              int32_t max_splits, int32_t* work_counter_dev, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, float* st_m, float* st_l, float* st_o) {
   SplitArgs a{};
   a.q = q;
   a.k_pool = k_pool;
@@ -340,21 +328,12 @@ extern "C" pkv_status pkv_decode_selfplan(const pkv_problem* prob, const int32_t
   a.bucket_row0 = -1;
   a.num_rows = prob->batch;
   a.work_counter = work_counter_dev;
-  // The persistent grid of pkv_decode_device.
-  const int per_cu = persistent_per_cu(prob);
-  const int64_t upper = int64_t(prob->batch) * prob->num_kv_heads * max_splits;
-  const int grid = static_cast<int>(std::min<int64_t>(upper, int64_t(per_cu) * cus));
-  a.num_items = grid;
-  return launch_split(*prob, kModeLens, prob->kernel, a, grid, stream);
+  return a;
 }
 
-extern "C" pkv_status pkv_merge_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
-                                         int32_t max_splits, int32_t* work_counter_dev,
-                                         const float* st_m, const float* st_l, const float* st_o,
-                                         void* out, float* lse, hipStream_t stream) {
-  pkv_status st = check_selfplan(prob, seq_lens_dev, max_splits, work_counter_dev);
-  if (st != PKV_OK) return st;
-  if (!st_m || !st_l || !st_o || !out) return PKV_EINVAL;
+MergeArgs selfplan_merge_args(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                              int32_t max_splits, int32_t* work_counter_dev, const float* st_m,
+                              const float* st_l, const float* st_o, void* out, float* lse) {
   MergeArgs a{};
   a.st_m = st_m;
   a.st_l = st_l;
@@ -370,6 +349,44 @@ extern "C" pkv_status pkv_merge_selfplan(const pkv_problem* prob, const int32_t*
   a.seq_lens = seq_lens_dev;
   a.max_pages = prob->max_pages_per_row;
   a.work_counter = work_counter_dev;  // the merge resets the split kernel's counter
+  return a;
+}
+
+}  // namespace pkv
+
+extern "C" pkv_status pkv_decode_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                                          int32_t max_splits, int32_t* work_counter_dev,
+                                          const void* q, const void* k_pool, const void* v_pool,
+                                          const int32_t* block_table, float* st_m, float* st_l,
+                                          float* st_o, hipStream_t stream) {
+  pkv_status st = check_selfplan_step(prob, seq_lens_dev, max_splits);
+  if (st != PKV_OK) return st;
+  if (!work_counter_dev) return PKV_EINVAL;
+  if (!q || !k_pool || !v_pool || !block_table || !st_m || !st_l || !st_o) return PKV_EINVAL;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return PKV_EHIP;
+  SplitArgs a = selfplan_split_args(prob, seq_lens_dev, max_splits, work_counter_dev, q, k_pool,
+                                    v_pool, block_table, st_m, st_l, st_o);
+  // The persistent grid of pkv_decode_device.
+  const int per_cu = persistent_per_cu(prob);
+  const int64_t upper = int64_t(prob->batch) * prob->num_kv_heads * max_splits;
+  const int grid = static_cast<int>(std::min<int64_t>(upper, int64_t(per_cu) * cus));
+  a.num_items = grid;
+  return launch_split(*prob, kModeLens, prob->kernel, a, grid, stream);
+}
+
+extern "C" pkv_status pkv_merge_selfplan(const pkv_problem* prob, const int32_t* seq_lens_dev,
+                                         int32_t max_splits, int32_t* work_counter_dev,
+                                         const float* st_m, const float* st_l, const float* st_o,
+                                         void* out, float* lse, hipStream_t stream) {
+  pkv_status st = check_selfplan_step(prob, seq_lens_dev, max_splits);
+  if (st != PKV_OK) return st;
+  if (!work_counter_dev) return PKV_EINVAL;
+  if (!st_m || !st_l || !st_o || !out) return PKV_EINVAL;
+  MergeArgs a = selfplan_merge_args(prob, seq_lens_dev, max_splits, work_counter_dev, st_m, st_l,
+                                    st_o, out, lse);
   return launch_merge(*prob, a, stream);
 }
 

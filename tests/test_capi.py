@@ -361,3 +361,26 @@ def test_probe_library_exports_its_header():
     assert declared == set(probe.EXPORTED)
     for name in declared:
         assert hasattr(probe.LIB, name), name
+
+
+def test_noalloc_scratch_size_and_limit():
+    """pkv_noalloc_bytes is the closed form (three 256-byte aligned arrays of
+    B * Hkv * S slots: m and l of G floats, o of G * d floats); a call needing
+    more than the library's array fails with PKV_ENOSPC before any GPU work."""
+    prob = _prob(8, hq=32, hkv=8, d=128)
+    slots, g = 8 * 8 * 32, 4
+
+    def r256(n):
+        return (n + 255) // 256 * 256
+
+    assert _lib.pkv_noalloc_bytes(prob, 32) == 2 * r256(slots * g * 4) + r256(slots * g * 128 * 4)
+    assert _lib.pkv_noalloc_bytes(prob, 0) == 0
+    big = _prob(1024, hq=64, hkv=8, d=128)
+    assert _lib.pkv_noalloc_bytes(big, 64) > _lib.PKV_NOALLOC_SCRATCH_BYTES
+    fake = 4096
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_attend_noalloc(big, fake, 64, fake, fake, fake, fake, fake, fake)
+    assert e.value.status == PKV_ENOSPC
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_attend_noalloc(prob, fake, 32, fake, fake, fake, fake, None, fake)
+    assert e.value.status == PKV_EINVAL
