@@ -24,7 +24,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [
     "planner.cpp", "api.cpp", "merge.hip", "split_valu.hip", "split_mfma.hip", "planner_device.hip",
-    "append.hip", "cost_model.cpp", "noalloc.hip",
+    "append.hip", "cost_model.cpp", "noalloc.hip", "noalloc_api.cpp",
 ]
 PROBE_SOURCES = ["read_probe.hip"]
 

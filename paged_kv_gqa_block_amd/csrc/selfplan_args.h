@@ -1,5 +1,5 @@
 // Host-side helpers of the self-planned step shared by api.cpp and
-// noalloc.hip.  Not part of the public ABI (see include/pkv.h).
+// noalloc_api.cpp.  Not part of the public ABI (see include/pkv.h).
 #pragma once
 
 #include "pkv_internal.h"
@@ -18,5 +18,9 @@ SplitArgs selfplan_split_args(const pkv_problem* prob, const int32_t* seq_lens_d
 MergeArgs selfplan_merge_args(const pkv_problem* prob, const int32_t* seq_lens_dev,
                               int32_t max_splits, int32_t* work_counter_dev, const float* st_m,
                               const float* st_l, const float* st_o, void* out, float* lse);
+
+// Device address of the allocation-free step's scratch array on the current
+// device (noalloc.hip; looked up on the first call per device).
+pkv_status noalloc_scratch_address(void** out);
 
 }  // namespace pkv

@@ -2,8 +2,9 @@
 
     python tests/sanitize/build_sanitized.py   -> tests/sanitize/_build/libpkv_san.so
 
-The host translation units (planner.cpp, cost_model.cpp, api.cpp) are
-compiled with g++ and linked with stub kernel launchers (stub_launchers.cpp)
+The host translation units (planner.cpp, cost_model.cpp, api.cpp,
+noalloc_api.cpp) are compiled with g++ and linked with stub kernel launchers
+and a stub scratch-address lookup (stub_launchers.cpp)
 against the HIP runtime; no device code is built.  Load the result through
 the binding by setting PKV_LIBRARY to its path and preloading the ASan
 runtime (see tests/test_sanitized_host.py).
@@ -20,7 +21,8 @@ CSRC = os.path.join(ROOT, "paged_kv_gqa_block_amd", "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libpkv_san.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
-SOURCES = [os.path.join(CSRC, f) for f in ("planner.cpp", "cost_model.cpp", "api.cpp")] + \
+SOURCES = [os.path.join(CSRC, f) for f in ("planner.cpp", "cost_model.cpp", "api.cpp",
+                                                   "noalloc_api.cpp")] + \
     [os.path.join(HERE, "stub_launchers.cpp")]
 FLAGS = ["-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
          "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",

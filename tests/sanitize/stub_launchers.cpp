@@ -7,6 +7,7 @@
 // an error instead of running anything.  The CPU tests that run against this
 // build exercise planning, policies, cost features and argument validation.
 #include "pkv_internal.h"
+#include "selfplan_args.h"
 
 namespace pkv {
 
@@ -19,5 +20,7 @@ pkv_status launch_plan_device(const pkv_problem&, const int32_t*, int32_t, int32
                               hipStream_t) {
   return PKV_EHIP;
 }
+// The allocation-free step's device array is not part of this build.
+pkv_status noalloc_scratch_address(void**) { return PKV_EHIP; }
 
 }  // namespace pkv
