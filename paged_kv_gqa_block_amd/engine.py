@@ -85,6 +85,27 @@ class DecodeStep:
         self.merge(stream)
         return self.out, self.lse
 
+    def bind(self, w: dict, stream=None) -> tuple:
+        """pkv_decode and pkv_merge of this step on workload buffers `w`, with
+        their arguments marshalled once (see ``run_bound``)."""
+        st = stream if stream is not None else torch.cuda.current_stream()
+        dec = _lib.bind_call("pkv_decode", self.prob, self.plan_host, self.plan_dev, w["q"],
+                             w["k_pool"], w["v_pool"], w["block_table"], w["seq_lens"],
+                             self.st_m, self.st_l, self.st_o, self.out, self.lse, st)
+        mrg = _lib.bind_call("pkv_merge", self.prob, self.plan_host, self.plan_dev, self.st_m,
+                             self.st_l, self.st_o, self.out, self.lse, st)
+        return dec, mrg
+
+    def run_bound(self, bound: tuple) -> None:
+        """The same two calls as ``run`` with pre-marshalled arguments: the
+        host enqueues a step in a few microseconds, so timing loops of short
+        steps measure the device, not the Python binding."""
+        _lib.call_bound(bound[0])
+        _lib.call_bound(bound[1])
+
+    def decode_bound(self, bound: tuple) -> None:
+        _lib.call_bound(bound[0])
+
 
 class _PersistentStepBuffers:
     """Output and partial-state buffers of a persistent-grid workqueue step

@@ -39,17 +39,30 @@ def pool_copies(wd: dict, copies_gib: float, max_copies: int = 64):
     return views
 
 
+def _capture(fn, stream) -> torch.cuda.CUDAGraph:
+    """A HIP graph of the launches fn() enqueues on `stream`."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    return g
+
+
 def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", steps: int = 50,
-              warmup: int = 10, sync_reps: int = 20, repeats: int = 5) -> dict:
+              warmup: int = 10, sync_reps: int = 20, repeats: int = 5,
+              graph: bool = False) -> dict:
     """Times one (path, split cap).  Returns step / split times and counters.
 
     The timed loops run `repeats` times; the reported step and split times are
     the medians (short kernels vary by several percent from run to run).
+    With ``graph``, the timed loop of K steps (and of K split launches) is
+    captured once in a HIP graph, launched once untimed (its first launch also
+    uploads it), and replayed: the same launches, enqueued by one graph launch
+    instead of one host call per kernel.
     """
     wd = views[0]
     prob = engine.problem_from_workload(w, kernel)
     step = engine.DecodeStep(prob, path, splits)
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream() if graph else torch.cuda.current_stream()
     info = step.plan(wd["seq_lens_host"], stream=stream)
     n = len(views)
     torch.cuda.synchronize()
@@ -57,28 +70,54 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         step.run(views[i % n], stream)
     torch.cuda.synchronize()
 
+    # Arguments marshalled once per pool copy: the host then enqueues a step
+    # in a few microseconds, well under the device time of the shortest steps.
+    bound = [step.bind(v, stream) for v in views]
+
+    def steps_from(base):
+        for i in range(steps):
+            step.run_bound(bound[(base + i) % n])
+
+    def splits_from(base):
+        for i in range(steps):
+            step.decode_bound(bound[(base + i) % n])
+
+    graphs = None
+    if graph:
+        # Captured once; the first launch of a graph also uploads it to the
+        # device, so each is launched once untimed before the timed replays.
+        graphs = (_capture(lambda: steps_from(warmup), stream),
+                  _capture(lambda: splits_from(warmup + steps), stream))
+        with torch.cuda.stream(stream):  # replays run on the capture stream
+            for g in graphs:
+                g.replay()
+        torch.cuda.synchronize()
     step_runs, split_runs, walls = [], [], []
     for rep in range(repeats):
-        # K back-to-back steps between two events (no event between launches).
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         base = warmup + rep * 2 * steps
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for i in range(steps):
-            step.run(views[(base + i) % n], stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        walls.append(time.perf_counter() - t0)
-        step_runs.append(1e3 * e0.elapsed_time(e1) / steps)
+        if graphs is not None:
+            run_steps, run_splits = graphs[0].replay, graphs[1].replay
+        else:
+            run_steps = lambda: steps_from(base)  # noqa: E731
+            run_splits = lambda: splits_from(base + steps)  # noqa: E731
+        # K back-to-back steps between two events (no event between launches).
+        with torch.cuda.stream(stream):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            run_steps()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t0)
+            step_runs.append(1e3 * e0.elapsed_time(e1) / steps)
 
-        # Split launches alone, back to back, so event overhead is amortised.
-        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e2.record(stream)
-        for i in range(steps):
-            step.decode(views[(base + steps + i) % n], stream)
-        e3.record(stream)
-        torch.cuda.synchronize()
-        split_runs.append(1e3 * e2.elapsed_time(e3) / steps)
+            # Split launches alone, back to back, so event overhead is amortised.
+            e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e2.record(stream)
+            run_splits()
+            e3.record(stream)
+            torch.cuda.synchronize()
+            split_runs.append(1e3 * e2.elapsed_time(e3) / steps)
     step_us = statistics.median(step_runs)
     split_us = statistics.median(split_runs)
     wall = statistics.median(walls)
@@ -88,10 +127,11 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
     # throughput figures above come from the back-to-back loops).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        step.run(views[(warmup + i) % n], stream)
-        b.record(stream)
+    with torch.cuda.stream(stream):
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            step.run(views[(warmup + i) % n], stream)
+            b.record(stream)
     torch.cuda.synchronize()
     single = sorted(1e3 * a.elapsed_time(b) for a, b in evs)
 
@@ -118,6 +158,7 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         "step_us": step_us,
         "split_us": split_us,
         "step_us_runs": [round(x, 2) for x in step_runs],
+        "launch": "graph" if graph else "eager",
         "single_step_us": {"p10": round(pct(0.1), 2), "p50": round(pct(0.5), 2),
                            "p90": round(pct(0.9), 2), "n": len(single)},
         "wall_ms_per_step": 1e3 * wall / steps,
@@ -130,37 +171,52 @@ def time_paths_interleaved(w: dict, views, configs, kernel: str = "auto", steps:
                            warmup: int = 5, repeats: int = 7, return_runs: bool = False):
     """Step time of several (path, split cap) configurations of one workload.
 
-    The timed loops alternate between the configurations (repeat r of every
-    configuration before repeat r + 1 of any), so a drift of the GPU's clock
-    during the measurement moves all of them alike; each result is the median
+    Each configuration's K steps (rotating over the pool copies) are captured
+    once in a HIP graph and replayed per timed repeat, so the host, whose
+    eager launches cost a few microseconds each, never holds the device back
+    on short steps.  The timed repeats alternate between the configurations
+    (repeat r of every configuration before repeat r + 1 of any), so a drift
+    of the GPU's clock moves all of them alike; each result is the median
     over its repeats.  Returns {"path:splits": step_us}, and with
-    ``return_runs`` also {"path:splits": [µs of each repeat]}.
+    ``return_runs`` also {"path:splits": [µs of each repeat]} and the host
+    time to launch one replay, per step.
     """
     prob = engine.problem_from_workload(w, kernel)
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream()
     n = len(views)
     steps_by = {}
     for path, s in configs:
         st = engine.DecodeStep(prob, path, s)
         st.plan(views[0]["seq_lens_host"], stream=stream)
+        bound = [st.bind(v, stream) for v in views]  # arguments marshalled once
         for i in range(warmup):
-            st.run(views[i % n], stream)
-        steps_by[f"{path}:{s}"] = st
+            st.run_bound(bound[i % n])
+        torch.cuda.synchronize()
+        graph = _capture(lambda st=st, bound=bound: [st.run_bound(bound[i % n])
+                                                       for i in range(steps)], stream)
+        with torch.cuda.stream(stream):
+            graph.replay()  # the first launch also uploads the graph: untimed
+        torch.cuda.synchronize()
+        steps_by[f"{path}:{s}"] = (st, graph)
     torch.cuda.synchronize()
     runs = {k: [] for k in steps_by}
-    k0 = 0
-    for _rep in range(repeats):
-        for key, st in steps_by.items():
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(steps):
-                st.run(views[(k0 + i) % n], stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            runs[key].append(1e3 * e0.elapsed_time(e1) / steps)
-            k0 += steps
+    host = {k: [] for k in steps_by}
+    with torch.cuda.stream(stream):
+        for _rep in range(repeats):
+            for key, (_st, graph) in steps_by.items():
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                t0 = time.perf_counter()
+                graph.replay()
+                host[key].append((time.perf_counter() - t0) * 1e6 / steps)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                runs[key].append(1e3 * e0.elapsed_time(e1) / steps)
     med = {k: statistics.median(v) for k, v in runs.items()}
-    return (med, runs) if return_runs else med
+    if return_runs:
+        return med, runs, {k: statistics.median(v) for k, v in host.items()}
+    return med
 
 
 def time_read_probe(w: dict, views, path: str, splits: int, steps: int = 50,
