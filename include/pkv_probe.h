@@ -42,6 +42,48 @@ int pkv_probe_read(const void* k_pool, const void* v_pool, const int32_t* block_
                    const void* plan_host, const void* plan_dev, uint32_t* sink,
                    hipStream_t stream);
 
+/*
+ * pkv_probe_read_lds: the same pages as pkv_probe_read (head_dim 128 only),
+ * moved by gfx950's buffer loads that write LDS directly.  Each of `waves`
+ * waves per workgroup keeps a ring of `depth` page slices (K 4 KiB + V 4 KiB)
+ * in LDS, so deep prefetch costs LDS (waves * depth * 8 KiB per workgroup)
+ * instead of registers.  With consume != 0 each page is read back from LDS
+ * before its slot is reloaded and folded into sink[(task * waves + wave) * 64
+ * + lane]: the sum, over that wave's pages (page_begin + wave, + waves, ...),
+ * of the xor of the four 32-bit words the lane read from each of the page's
+ * eight 16-byte chunks (K then V, chunk i at byte offset i * 1024 + lane * 16
+ * of the 4 KiB slice); with consume == 0 that entry is 0.  sink holds at
+ * least n_tasks * waves * 64 uint32.  Supported (waves, depth): (4, 2),
+ * (4, 4), (8, 2), (2, 7).  Other arguments and the return codes as for
+ * pkv_probe_read.
+ */
+int pkv_probe_read_lds(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                       int32_t max_pages_per_row, int32_t num_kv_heads, int32_t head_dim,
+                       const void* plan_host, const void* plan_dev, int32_t waves,
+                       int32_t depth, int32_t consume, uint32_t* sink, hipStream_t stream);
+
+/*
+ * pkv_probe_stream: a contiguous streaming read of `bytes` bytes of device
+ * memory at `buf` (the rate HBM gives a plain sequential reader of the same
+ * byte count, with no block table): `grid` workgroups of 256 threads each read
+ * one contiguous chunk of bytes / grid, 16-byte non-temporal loads,
+ * loads_in_flight (4 or 8) per thread.  bytes must be a multiple of
+ * grid * 4096 * loads_in_flight, and bytes / grid below 2^31.  sink: at least
+ * `grid` uint32, written only in a case that never happens for finite data.
+ * Returns 0, -1 for bad arguments, -6 when the launch fails.
+ */
+int pkv_probe_stream(const void* buf, int64_t bytes, int32_t grid, int32_t loads_in_flight,
+                     uint32_t* sink, hipStream_t stream);
+
+/*
+ * pkv_probe_empty: a kernel of `grid` workgroups of `threads` threads that
+ * does nothing but, when flag is not NULL, copy flag[0] to flag[1] (one
+ * thread).  Launched after a split kernel with the merge's grid, it measures
+ * what a dependent launch costs by itself.  Returns 0, -1 for bad sizes, -6
+ * when the launch fails.
+ */
+int pkv_probe_empty(int32_t grid, int32_t threads, uint32_t* flag, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
