@@ -1,7 +1,8 @@
 """Decode-attention benchmark: µs per decode step and achieved HBM GB/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
-                    [--path bucketed|workqueue|nosplit|padded|policy|model|device|selfplan] [--kernel auto|valu|mfma]
+                    [--path bucketed|workqueue|nosplit|padded|policy|model|default|device|selfplan]
+                    [--kernel auto|valu|mfma] [--launch graph|eager]
 
 One step is the engine's device work for one decode step of one layer: the
 split kernel launch(es) and the merge launch(es) (or the single no-split
@@ -9,7 +10,14 @@ launch), with the plan already resident on the GPU.  Inputs are generated
 (seeded, synthetic) and copied to HBM before timing.  To keep the 256 MB
 Infinity Cache from serving K/V, every step reads a different copy of the KV
 pools (as consecutive layers of a model would), with enough copies to exceed
-1 GiB.
+1 GiB.  By default the K timed steps are launched eagerly, back to back (the
+host enqueues a kernel in a few microseconds, well under the device time of
+these steps); with --launch graph they are captured once in a HIP graph,
+launched once untimed and then replayed.  The line also reports the same K
+steps launched the other way (on these device-bound steps graph replay is
+0-2 us per step slower, the short launch-bound steps of the policy sweep are
+where it pays).  For the long and bimodal workloads the line carries
+both target workloads' figures in `targets`.
 
 Printed JSON line: value = real-KV bytes (sum N_i * Hkv * d * 2 * 2) divided by
 the device step time measured with HIP events on the launch stream.  The
@@ -59,6 +67,14 @@ def parse_args(argv=None):
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--copies-gib", type=float, default=1.0,
                    help="total size of the rotated KV pool copies")
+    p.add_argument("--launch", choices=("graph", "eager"), default="eager",
+                   help="graph: the K timed steps are captured once in a HIP "
+                        "graph, launched once untimed, then replayed -- device time, as a "
+                        "serving loop that replays its decode graph sees it; eager (the "
+                        "default): one host "
+                        "call per kernel")
+    p.add_argument("--no-targets", action="store_true",
+                   help="skip the second target workload's figures")
     p.add_argument("--all", action="store_true",
                    help="instead of the single contract line, print one JSON line per "
                         "(workload, path) for every workload, each with a short CPU-oracle "
@@ -181,9 +197,10 @@ def run_all(args) -> int:
         views = timing.pool_copies(wd, args.copies_gib, max_copies=8)
         pol = engine.choose(rules, spec.batch, int(lens.max()))
         mod = engine.choose_model(cost_model, engine.problem_from_workload(w), lens)[:2]
+        dflt = engine.choose_default(rules, cost_model, engine.problem_from_workload(w), lens)
         cands = [("bucketed", spec.splits), ("workqueue", spec.splits), ("nosplit", 1),
                  ("padded", spec.splits)]
-        for c in (pol, mod):
+        for c in (pol, mod, dflt):
             if c not in cands:
                 cands.append(c)
         cpu = None if args.no_cpu_baseline else cpu_baseline(w, min(args.cpu_budget_s, 5.0))
@@ -211,12 +228,13 @@ def run_all(args) -> int:
                     "cpu_oracle": None}), flush=True)
         for path, s in cands:
             r = timing.time_path(w, views, path, s, args.kernel, args.steps, args.warmup,
-                                 sync_reps=5)
+                                 sync_reps=5, graph=args.launch == "graph")
             kv = r["info"]["kv_bytes"]
             gbs = kv / (r["step_us"] * 1e-6) / 1e9
             print(json.dumps({
                 "workload": describe(spec, path, s, lens), "config": name, "path": path,
                 "splits": s, "policy_choice": (path, s) == pol, "model_choice": (path, s) == mod,
+                "default_choice": (path, s) == dflt, "launch": r["launch"],
                 "us_per_step": round(r["step_us"], 2), "GB/s": round(gbs, 1),
                 "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                 "single_step_us": r["single_step_us"],
@@ -258,65 +276,55 @@ def run_device(args, spec, seed, splits, w, wd, lens, selfplan=False) -> int:
     return 0
 
 
-def main(argv=None):
-    args = parse_args(argv)
-    if args.gpus != 1:
-        print(f"bench.py: this engine runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the decode path has no multi-GPU mode)", file=sys.stderr)
-        return 2
-    import numpy as np
-    import torch
+# The two workloads the 70 %-of-peak target is quoted on: the long single row
+# (length-bucketed split path) and the bimodal batch (compact workqueue, up to
+# 32 splits per row).
+TARGETS = ("long", "bimodal")
 
-    from paged_kv_gqa_block_amd import engine, timing, traces
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.all:
-        return run_all(args)
-    spec = traces.get_spec(args.config)
-    seed = traces.HELD_OUT_SEED if args.seed is None else args.seed
-    path = args.path or DEFAULT_PATH.get(args.config, "workqueue")
+def choose_path(args, spec, w, lens):
+    """(path, splits) of a workload: --path / --splits, else its default."""
+    from paged_kv_gqa_block_amd import engine
+
+    path = args.path or DEFAULT_PATH.get(spec.name, "workqueue")
     splits = args.splits or spec.splits
-    w = traces.generate(spec, seed)
-    lens = w["seq_lens"].numpy()
-    if path == "policy":
-        rules = engine.load_policy_table()
-        path, splits = engine.choose(rules, spec.batch, int(lens.max()))
+    if path == "policy":  # the calibrated (B, N_max) table
+        path, splits = engine.choose(engine.load_policy_table(), spec.batch, int(lens.max()))
     elif path == "model":  # the learned cost model's choice
         path, splits, _ = engine.choose_model(engine.load_cost_model(),
                                               engine.problem_from_workload(w), lens)
-    wd = engine.to_device(w)
-    engine.validate_inputs(wd)
-    if path in ("device", "selfplan"):
-        return run_device(args, spec, seed, splits, w, wd, lens, selfplan=path == "selfplan")
+    elif path == "default":  # the engine's default policy (table for B = 1, model else)
+        path, splits = engine.choose_default(engine.load_policy_table(),
+                                             engine.load_cost_model(),
+                                             engine.problem_from_workload(w), lens)
+    return path, splits
 
+
+def measure(args, w, wd, path, splits, seed, with_probe=True):
+    """One workload in one launch configuration: the contract figures (K steps
+    timed once) and the split kernel's roofline."""
+    from paged_kv_gqa_block_amd import timing
+
+    spec = w["spec"]
+    lens = w["seq_lens"].numpy()
     kernel_used = args.kernel
     if kernel_used == "auto":  # the library's AUTO rule: matrix cores for d = 128
         kernel_used = "mfma" if spec.head_dim == 128 else "valu"
     views = timing.pool_copies(wd, args.copies_gib)
-    # The contract line times exactly K steps once (repeats=1).
-    r = timing.time_path(w, views, path, splits, args.kernel, args.steps, args.warmup, repeats=1)
+    # Exactly K steps timed once (repeats=1), launched as configured.
+    r = timing.time_path(w, views, path, splits, args.kernel, args.steps, args.warmup, repeats=1,
+                         graph=args.launch == "graph")
     info = r["info"]
     kv = info["kv_bytes"]
     gbs = kv / (r["step_us"] * 1e-6) / 1e9
     split_launch_us = r["split_us"] / max(1, r["n_split_launches"])
     split_gbs = (kv / max(1, r["n_split_launches"])) / (split_launch_us * 1e-6) / 1e9
-    line = {
-        "metric": METRIC,
-        "value": round(gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(r["wall_ms_per_step"], 4),
-        "us_per_step": round(r["step_us"], 2),
+    out = {
+        "us_per_step": round(r["step_us"], 2), "GB/s": round(gbs, 1),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": spec.dtype,
-        "data": "synthetic",
+        "wall_ms_per_step": r["wall_ms_per_step"],
         "config": {"workload": describe(spec, path, splits, lens), "seed": seed,
-                   "kernel": args.kernel, "path": path, "splits": splits,
+                   "kernel": args.kernel, "path": path, "splits": splits, "launch": r["launch"],
                    "launches_per_step": info["n_launches"], "n_tasks": info["n_tasks"],
                    "kv_bytes": kv, "merge_state_bytes": info["merge_state_bytes"],
                    "pool_copies_rotated": len(views),
@@ -324,18 +332,94 @@ def main(argv=None):
                    "sync_wall_us_incl_plan": round(r["sync_wall_us_median"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.config, kernel_used, path, splits, seed),
+                     "traffic": recorded_traffic(spec.name, kernel_used, path, splits, seed),
                      "kernel": f"split decode ({kernel_used})",
                      "launch_us": round(split_launch_us, 2),
                      "algorithmic_bytes_per_launch": kv // max(1, r["n_split_launches"])},
     }
-    if r["n_split_launches"] == 1:
+    # The same K steps launched the other way, for comparison.
+    other = timing.time_path(w, views, path, splits, args.kernel, args.steps, args.warmup,
+                             repeats=1, sync_reps=0, graph=args.launch != "graph")
+    out["config"][f"{other['launch']}_us_per_step"] = round(other["step_us"], 2)
+    if with_probe and r["n_split_launches"] == 1:
         # The same tasks' pages streamed by a read-only kernel: the rate this
         # access pattern reaches on the device (the split kernel's ceiling).
         pr = timing.time_read_probe(w, views, path, splits, args.steps, args.warmup)
-        line["roofline"]["read_only_probe"] = {
+        out["roofline"]["read_only_probe"] = {
             "GB/s": round(pr["GB/s"], 1), "launch_us": round(pr["us_per_launch"], 2),
             "achieved_over_probe": round(split_gbs / pr["GB/s"], 4)}
+    return out
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this engine runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path has no multi-GPU mode)", file=sys.stderr)
+        return 2
+    import torch
+
+    from paged_kv_gqa_block_amd import engine, traces
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.all:
+        return run_all(args)
+    spec = traces.get_spec(args.config)
+    seed = traces.HELD_OUT_SEED if args.seed is None else args.seed
+    w = traces.generate(spec, seed)
+    lens = w["seq_lens"].numpy()
+    path, splits = choose_path(args, spec, w, lens)
+    wd = engine.to_device(w)
+    engine.validate_inputs(wd)
+    if path in ("device", "selfplan"):
+        return run_device(args, spec, seed, splits, w, wd, lens, selfplan=path == "selfplan")
+
+    m = measure(args, w, wd, path, splits, seed)
+    line = {
+        "metric": METRIC,
+        "value": m["GB/s"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["wall_ms_per_step"], 4),
+        "us_per_step": m["us_per_step"],
+        "pct_of_peak": m["pct_of_peak"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": m["config"],
+        "roofline": m["roofline"],
+    }
+    if args.config in TARGETS and not args.no_targets:
+        # Both target workloads in their default launch configuration, on the
+        # same held-out seed and rotated pools.
+        targets = {}
+        for name in TARGETS:
+            if name == args.config and args.path is None and args.splits is None:
+                t = m
+            else:
+                del wd
+                torch.cuda.empty_cache()
+                tspec = traces.get_spec(name)
+                w = traces.generate(tspec, seed)
+                wd = engine.to_device(w)
+                engine.validate_inputs(wd)
+                tp = DEFAULT_PATH.get(name, "workqueue")
+                t = measure(args, w, wd, tp, tspec.splits, seed)
+            targets[name] = {"us_per_step": t["us_per_step"], "GB/s": t["GB/s"],
+                             "pct_of_peak": t["pct_of_peak"],
+                             "workload": t["config"]["workload"],
+                             "launch": t["config"]["launch"],
+                             "graph_us_per_step": t["config"].get("graph_us_per_step"),
+                             "eager_us_per_step": t["config"].get("eager_us_per_step"),
+                             "split_roofline": {k: t["roofline"][k] for k in
+                                                ("achieved", "frac", "launch_us", "traffic")},
+                             "read_only_probe": t["roofline"].get("read_only_probe")}
+        line["targets"] = targets
+        w = traces.generate(spec, seed)  # the contract workload again, for the CPU leg
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
