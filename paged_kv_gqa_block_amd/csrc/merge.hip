@@ -21,8 +21,23 @@
 namespace pkv {
 namespace {
 
+// Brings every argument field the merge reads into scalar registers at
+// entry.  A field's first read is a scalar load from the argument segment,
+// which the caches do not hold across launches (about 0.6 us each); loaded
+// where they are first used, the fields arrived in three round trips one
+// after the other.  Used together here, they are issued back to back and
+// waited for once (measured on MI355X: 0.4-0.7 us less per step).
+__device__ __forceinline__ void args_in_registers(const MergeArgs& a) {
+  asm volatile("" ::"s"(a.st_m), "s"(a.st_l), "s"(a.st_o), "s"(a.row_nsplit),
+               "s"(a.row_task_off), "s"(a.bucket_rows), "s"(a.out), "s"(a.lse),
+               "s"(a.num_q_heads), "s"(a.num_kv_heads), "s"(a.group), "s"(a.splits),
+               "s"(a.num_rows), "s"(a.mode), "s"(a.bucket_row0), "s"(a.device_plan),
+               "s"(a.uniform_nsplit), "s"(a.seq_lens), "s"(a.max_pages), "s"(a.work_counter));
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  args_in_registers(a);
   constexpr int CH = D / 4;    // float4 chunks per output row
   constexpr int SG = 256 / CH; // split groups
   constexpr int U = 4;         // states loaded per thread per round
