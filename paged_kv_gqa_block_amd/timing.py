@@ -274,6 +274,9 @@ def time_device_path(w: dict, views, splits: int, steps: int = 50, warmup: int =
             with torch.cuda.graph(g, stream=stream):
                 step.run(v, stream)
             graphs.append(g)
+        with torch.cuda.stream(stream):  # the first launch also uploads a graph: untimed
+            for g in graphs:
+                g.replay()
         torch.cuda.synchronize()
 
     def one(i):
