@@ -143,35 +143,49 @@ __device__ __forceinline__ void write_empty_row(const SplitArgs& a, const Task& 
 // Combine the NW waves' states (max in log2 units, sum, unnormalised output,
 // already in LDS) and write either the task's partial state or, on the
 // no-split path, the normalised output and lse.  Must follow a barrier.
+// Each thread combines four consecutive output elements of one head (one
+// 16-byte LDS read per wave, one 16-byte state store); per element the
+// arithmetic and its order are those of a one-element loop.  sm_o must be
+// 16-byte aligned.
 template <int D, int GP, int NW, bool BF16, int MODE>
 __device__ __forceinline__ void combine_waves_and_store(const SplitArgs& a, const Task& t, int G,
                                                         const float (&sm_m)[NW][GP],
                                                         const float (&sm_l)[NW][GP],
                                                         const float (&sm_o)[NW][GP][D]) {
-  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-    const int h = e / D;
-    const int dd = e - h * D;
+  constexpr int C4 = D / 4;  // 16-byte chunks per head
+  for (int e = threadIdx.x; e < G * C4; e += NW * 64) {
+    const int h = e / C4;
+    const int c4 = e - h * C4;
     float mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
-    float lsum = 0.f, osum = 0.f;
+    float lsum = 0.f;
+    float4 osum = make_float4(0.f, 0.f, 0.f, 0.f);
     if (mx != kNegInf) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float mw = sm_m[w][h];
         const float wt = (mw == kNegInf) ? 0.f : fast_exp2(mw - mx);
         lsum = fmaf(wt, sm_l[w][h], lsum);
-        osum = fmaf(wt, sm_o[w][h][dd], osum);
+        const float4 o = reinterpret_cast<const float4*>(sm_o[w][h])[c4];
+        osum.x = fmaf(wt, o.x, osum.x);
+        osum.y = fmaf(wt, o.y, osum.y);
+        osum.z = fmaf(wt, o.z, osum.z);
+        osum.w = fmaf(wt, o.w, osum.w);
       }
     }
     if constexpr (MODE == kModeNoSplit) {
       const int64_t qh = int64_t(t.row) * a.num_q_heads + t.g * G + h;
-      const float val = (lsum > 0.f) ? osum / lsum : 0.f;
-      static_cast<uint16_t*>(a.out)[qh * D + dd] = Elem<BF16>::from_float(val);
-      if (dd == 0 && a.lse) a.lse[qh] = (lsum > 0.f) ? mx * kLn2 + __logf(lsum) : kNegInf;
+      const bool pos = lsum > 0.f;
+      const uint32_t lo = uint32_t(Elem<BF16>::from_float(pos ? osum.x / lsum : 0.f)) |
+                          (uint32_t(Elem<BF16>::from_float(pos ? osum.y / lsum : 0.f)) << 16);
+      const uint32_t hi = uint32_t(Elem<BF16>::from_float(pos ? osum.z / lsum : 0.f)) |
+                          (uint32_t(Elem<BF16>::from_float(pos ? osum.w / lsum : 0.f)) << 16);
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + qh * D)[c4] = make_uint2(lo, hi);
+      if (c4 == 0 && a.lse) a.lse[qh] = pos ? mx * kLn2 + __logf(lsum) : kNegInf;
     } else {
-      a.st_o[(t.slot * G + h) * D + dd] = osum;
-      if (dd == 0) {
+      reinterpret_cast<float4*>(a.st_o + (t.slot * G + h) * D)[c4] = osum;
+      if (c4 == 0) {
         a.st_m[t.slot * G + h] = (mx == kNegInf) ? kNegInf : mx * kLn2;
         a.st_l[t.slot * G + h] = lsum;
       }

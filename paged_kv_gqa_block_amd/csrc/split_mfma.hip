@@ -128,7 +128,7 @@ template <int GP, int NW>
 struct MfmaShared {
   float m[NW][GP];
   float l[NW][GP];
-  float o[NW][GP][128];
+  alignas(16) float o[NW][GP][128];
   uint4 k[NW][16][16];  // per-wave K tile: [token][physical chunk]
 };
 

@@ -219,7 +219,7 @@ template <int D, int GP, bool BF16, int NW, int PF, int MODE>
 __global__ __launch_bounds__(NW * 64) void split_valu_kernel(SplitArgs a) {
   __shared__ float sm_m[NW][GP];
   __shared__ float sm_l[NW][GP];
-  __shared__ float sm_o[NW][GP][D];
+  __shared__ __align__(16) float sm_o[NW][GP][D];
   if constexpr (MODE == kModePersistent) {
     persistent_plan_loop(a, [&](const Task& tk) {
       valu_task<D, GP, BF16, NW, PF, kModeWorkqueue>(a, tk, sm_m, sm_l, sm_o);
