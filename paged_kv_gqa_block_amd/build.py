@@ -33,13 +33,16 @@ COMMON_FLAGS = [
     "-Wall", "-Wno-unused-result",
 ]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source additions.  merge.hip: leading scalar kernel parameters are
+# preloaded into SGPRs at wave launch (the small-grid merge kernel uses it).
+EXTRA_FLAGS = {"merge.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *COMMON_FLAGS]
     if src.endswith(".hip"):
-        cmd += ["-x", "hip", *DEVICE_FLAGS]
+        cmd += ["-x", "hip", *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, [])]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
