@@ -33,8 +33,8 @@ COMMON_FLAGS = [
     "-Wall", "-Wno-unused-result",
 ]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source additions.  merge.hip: leading scalar kernel parameters are
-# preloaded into SGPRs at wave launch (the small-grid merge kernel uses it).
+# Per-source additions.  merge.hip: the leading scalar kernel parameters
+# (14 dwords) are preloaded into SGPRs at wave launch.
 EXTRA_FLAGS = {"merge.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"]}
 
 

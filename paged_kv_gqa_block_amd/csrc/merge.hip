@@ -164,57 +164,32 @@ __device__ __forceinline__ void merge_body(const MergeHot& hot, const MergeArgs&
   if (a.lse && t == 0) a.lse[qh] = (lsum > 0.f) ? mx + __logf(lsum) : kNegInf;
 }
 
-// Brings every argument field the merge reads into scalar registers at
-// entry.  A field's first read is a scalar load from the argument segment,
-// which the caches do not hold across launches (about 0.6 us each); loaded
-// where they are first used, the fields arrived in three round trips one
-// after the other.  Used together here, they are issued back to back and
-// waited for once (measured on MI355X: 0.3-1.0 us less per step).
-__device__ __forceinline__ void args_in_registers(const MergeArgs& a) {
-  asm volatile("" ::"s"(a.st_m), "s"(a.st_l), "s"(a.st_o), "s"(a.row_nsplit),
-               "s"(a.row_task_off), "s"(a.bucket_rows), "s"(a.out), "s"(a.lse),
-               "s"(a.num_q_heads), "s"(a.num_kv_heads), "s"(a.group), "s"(a.splits),
-               "s"(a.num_rows), "s"(a.mode), "s"(a.bucket_row0), "s"(a.device_plan),
-               "s"(a.uniform_nsplit), "s"(a.seq_lens), "s"(a.max_pages), "s"(a.work_counter));
-}
-
+// The merge kernel.  The scalars the first state loads depend on (MergeHot)
+// are its leading parameters, which this file's kernel-argument preloading
+// puts into SGPRs at wave launch: a field read from the argument segment
+// instead costs a memory round trip (about 0.6 us on MI355X, the segment being
+// written for every launch), and loaded where first used the fields arrived
+// in three such round trips one after the other.  The remaining fields of `a`
+// (output, lse, plan arrays, counters) are needed later.  Measured on MI355X
+// (same-box A/B): 0.3-1.0 us less per step than the lazily loaded arguments
+// on every workload with a merge, up to 1.5 us at B = 64.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  args_in_registers(a);
-  merge_body<D, BF16>(MergeHot{a.st_m, a.st_l, a.st_o, a.num_q_heads, a.num_kv_heads, a.group,
-                               a.splits, a.bucket_row0, a.uniform_nsplit, a.mode, a.num_rows},
-                      a);
-}
-
-// The same merge with the scalars of MergeHot as leading kernel parameters.
-// This file is compiled with kernel-argument preloading: the hardware puts
-// those 14 dwords into scalar registers at wave launch, so the first state
-// loads wait on no memory; the remaining fields of `a` (output, lse, plan
-// arrays, counters) are loaded by the kernel and needed later.  Preloading
-// costs the dispatcher time per wave, so it pays only on small grids
-// (kPreloadMergeMaxItems; measured on MI355X: 0.3-0.5 us less per step at
-// B = 1, up to 0.3 us more at B = 8).
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void merge_kernel_preloaded(
-    const float* st_m, const float* st_l, const float* st_o, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t group, int32_t splits, int32_t bucket_row0,
-    int32_t uniform_nsplit, int32_t mode, int32_t num_rows, MergeArgs a) {
+__global__ __launch_bounds__(256) void merge_kernel(const float* st_m, const float* st_l,
+                                                    const float* st_o, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t group,
+                                                    int32_t splits, int32_t bucket_row0,
+                                                    int32_t uniform_nsplit, int32_t mode,
+                                                    int32_t num_rows, MergeArgs a) {
   merge_body<D, BF16>(MergeHot{st_m, st_l, st_o, num_q_heads, num_kv_heads, group, splits,
                                bucket_row0, uniform_nsplit, mode, num_rows},
                       a);
 }
 
-constexpr int64_t kPreloadMergeMaxItems = 128;
-
 template <int D, bool BF16>
 void launch_merge_kernel(const MergeArgs& a, int64_t items, hipStream_t s) {
-  const dim3 grid(static_cast<uint32_t>(items)), block(256);
-  if (items <= kPreloadMergeMaxItems)
-    hipLaunchKernelGGL((merge_kernel_preloaded<D, BF16>), grid, block, 0, s, a.st_m, a.st_l,
-                       a.st_o, a.num_q_heads, a.num_kv_heads, a.group, a.splits, a.bucket_row0,
-                       a.uniform_nsplit, a.mode, a.num_rows, a);
-  else
-    hipLaunchKernelGGL((merge_kernel<D, BF16>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<D, BF16>), dim3(static_cast<uint32_t>(items)), dim3(256), 0,
+                     s, a.st_m, a.st_l, a.st_o, a.num_q_heads, a.num_kv_heads, a.group, a.splits,
+                     a.bucket_row0, a.uniform_nsplit, a.mode, a.num_rows, a);
 }
 
 }  // namespace
