@@ -49,7 +49,7 @@ TRAFFIC_PROFILES = {"long": "profiles/split_mfma_long_b1_n32768_traffic.txt",
                     "policy_b64": "profiles/split_mfma_policy_b64_traffic.txt"}
 KERNEL_SOURCES = ("split_mfma.hip", "split_common.h", "device_common.h", "pkv_internal.h",
                   "lens_plan.h")
-DEFAULT_PATH = {"tiny": "workqueue", "long": "workqueue", "bimodal": "workqueue",
+DEFAULT_PATH = {"tiny": "workqueue", "long": "bucketed", "bimodal": "workqueue",
                 "zipf": "workqueue", "uniform": "workqueue"}
 
 
@@ -277,8 +277,8 @@ def run_device(args, spec, seed, splits, w, wd, lens, selfplan=False) -> int:
 
 
 # The two workloads the 70 %-of-peak target is quoted on: the long single row
-# and the bimodal batch, both on the compact workqueue with up to 32 splits
-# per row (the engine's default policy picks it for both).
+# on the length-bucketed split path and the bimodal batch on the compact
+# workqueue, both with up to 32 splits per row.
 TARGETS = ("long", "bimodal")
 
 

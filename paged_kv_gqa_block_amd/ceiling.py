@@ -1,6 +1,6 @@
 """Where a decode step's time goes: read ceilings and launch floors.
 
-    python -m paged_kv_gqa_block_amd.ceiling [--config long] [--path workqueue] [--splits 32]
+    python -m paged_kv_gqa_block_amd.ceiling [--config long] [--path bucketed] [--splits 32]
                                              [--steps 40] [--repeats 7]
 
 On one workload in one launch configuration, times loops of K launches, each
@@ -79,7 +79,7 @@ def _loops(w, views, step, bound, stream, kv_bytes, hq_rows):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--config", default="long")
-    ap.add_argument("--path", default="workqueue")
+    ap.add_argument("--path", default="bucketed")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
