@@ -84,6 +84,17 @@ int pkv_probe_stream(const void* buf, int64_t bytes, int32_t grid, int32_t loads
  */
 int pkv_probe_empty(int32_t grid, int32_t threads, uint32_t* flag, hipStream_t stream);
 
+/*
+ * pkv_probe_sleep: one wave that waits `microseconds` (0..50000) of the
+ * device's constant-rate clock (hipDeviceAttributeWallClockRate) and ends;
+ * it always ends, after at most a bounded number of sleep rounds.  Enqueued
+ * just before the start event of a timed window, it keeps the device busy
+ * while the host enqueues the window's launches, so the window measures the
+ * launches and not the host's first submission.  Returns 0, -1 for a bad
+ * duration, -6 when the clock rate cannot be read or the launch fails.
+ */
+int pkv_probe_sleep(int32_t microseconds, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -120,6 +120,7 @@ def main(argv=None) -> int:
             for name, g in graphs.items():
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
+                probe.probe_sleep(timing.LEAD_US, stream)
                 e0.record(stream)
                 g.replay()
                 e1.record(stream)

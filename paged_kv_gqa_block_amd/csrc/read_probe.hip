@@ -176,6 +176,19 @@ __global__ __launch_bounds__(256) void probe_stream_kernel(const uint8_t* __rest
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // keeps the loads; practically never true
 }
 
+// One wave that sleeps until `ticks` of the device's constant-rate clock
+// have passed since it started (at most kMaxSleepRounds sleeps of 127 x 64
+// cycles, so it always ends), then returns.  Enqueued before a timed window,
+// it keeps the device busy while the host enqueues the window's launches.
+constexpr int kMaxSleepRounds = 20000;
+__global__ void probe_sleep_kernel(uint64_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < kMaxSleepRounds; ++i) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(127);
+  }
+}
+
 // A kernel with (almost) no work: thread 0 of workgroup 0 copies flag[0] to
 // flag[1] when flag is given.  Launched after a split kernel with the merge's
 // grid it isolates the cost of a dependent launch.
@@ -254,5 +267,21 @@ extern "C" int pkv_probe_empty(int32_t grid, int32_t threads, uint32_t* flag,
                                hipStream_t stream) {
   if (grid < 1 || threads < 1 || threads > 1024) return -1;
   hipLaunchKernelGGL(probe_empty_kernel, dim3(grid), dim3(threads), 0, stream, flag);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+extern "C" int pkv_probe_sleep(int32_t microseconds, hipStream_t stream) {
+  if (microseconds < 0 || microseconds > 50000) return -1;
+  static int khz = 0;  // rate of the clock s_memrealtime reads (device 0's, as every MI355X's)
+  if (khz == 0) {
+    int dev = 0, rate = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        rate <= 0)
+      return -6;
+    khz = rate;
+  }
+  const uint64_t ticks = uint64_t(microseconds) * uint64_t(khz) / 1000u;
+  hipLaunchKernelGGL(probe_sleep_kernel, dim3(1), dim3(64), 0, stream, ticks);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }

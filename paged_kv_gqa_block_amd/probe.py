@@ -11,7 +11,8 @@ import torch
 from . import _lib  # loads torch's HIP runtime before the probe library
 
 PROBE_LIB_PATH = os.path.join(_lib.PKG_DIR, "libpkv_probe.so")
-EXPORTED = ("pkv_probe_read", "pkv_probe_read_lds", "pkv_probe_stream", "pkv_probe_empty")
+EXPORTED = ("pkv_probe_read", "pkv_probe_read_lds", "pkv_probe_stream", "pkv_probe_empty",
+            "pkv_probe_sleep")
 LDS_SHAPES = ((4, 2), (4, 4), (8, 2), (2, 7))  # (waves, pages in LDS per wave)
 
 if not os.path.exists(PROBE_LIB_PATH):
@@ -28,6 +29,8 @@ LIB.pkv_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
                                  ctypes.c_void_p, ctypes.c_void_p]
 LIB.pkv_probe_empty.restype = ctypes.c_int
 LIB.pkv_probe_empty.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+LIB.pkv_probe_sleep.restype = ctypes.c_int
+LIB.pkv_probe_sleep.argtypes = [ctypes.c_int32, ctypes.c_void_p]
 
 
 def probe_read(w: dict, step, sink: torch.Tensor, stream=None) -> None:
@@ -84,3 +87,10 @@ def probe_empty(grid: int, threads: int, flag=None, stream=None) -> None:
                              _stream_ptr(stream))
     if rc != 0:
         raise RuntimeError(f"pkv_probe_empty failed ({rc})")
+
+
+def probe_sleep(microseconds: int, stream=None) -> None:
+    """Keep the device busy for `microseconds` (enqueued before a timed window)."""
+    rc = LIB.pkv_probe_sleep(int(microseconds), _stream_ptr(stream))
+    if rc != 0:
+        raise RuntimeError(f"pkv_probe_sleep failed ({rc})")

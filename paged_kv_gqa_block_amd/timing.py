@@ -16,7 +16,12 @@ import time
 import numpy as np
 import torch
 
-from . import _lib, engine
+from . import _lib, engine, probe
+
+# Device time the host gets to enqueue a timed window before it starts: a
+# sleeping wave (pkv_probe_sleep) is enqueued just before the start event,
+# so the window holds the launches and not the host's first submission.
+LEAD_US = 200
 
 
 # MI355X's Infinity Cache (MALL) holds 256 MiB; the rotated copies always
@@ -92,7 +97,7 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
             for g in graphs:
                 g.replay()
         torch.cuda.synchronize()
-    step_runs, split_runs, walls = [], [], []
+    step_runs, split_runs = [], []
     for rep in range(repeats):
         base = warmup + rep * 2 * steps
         if graphs is not None:
@@ -103,16 +108,16 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         # K back-to-back steps between two events (no event between launches).
         with torch.cuda.stream(stream):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0 = time.perf_counter()
+            probe.probe_sleep(LEAD_US, stream)
             e0.record(stream)
             run_steps()
             e1.record(stream)
             torch.cuda.synchronize()
-            walls.append(time.perf_counter() - t0)
             step_runs.append(1e3 * e0.elapsed_time(e1) / steps)
 
             # Split launches alone, back to back, so event overhead is amortised.
             e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            probe.probe_sleep(LEAD_US, stream)
             e2.record(stream)
             run_splits()
             e3.record(stream)
@@ -120,7 +125,6 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
             split_runs.append(1e3 * e2.elapsed_time(e3) / steps)
     step_us = statistics.median(step_runs)
     split_us = statistics.median(split_runs)
-    wall = statistics.median(walls)
 
     # Distribution of single steps: an event pair around each step of one
     # more loop (the events add a little time to each step, so the
@@ -161,7 +165,6 @@ def time_path(w: dict, views, path: str, splits: int, kernel: str = "auto", step
         "launch": "graph" if graph else "eager",
         "single_step_us": {"p10": round(pct(0.1), 2), "p50": round(pct(0.5), 2),
                            "p90": round(pct(0.9), 2), "n": len(single)},
-        "wall_ms_per_step": 1e3 * wall / steps,
         "sync_wall_us_median": statistics.median(sync_us) if sync_us else None,
         "out": step.out,
     }
@@ -206,6 +209,7 @@ def time_paths_interleaved(w: dict, views, configs, kernel: str = "auto", steps:
             for key, (_st, graph) in steps_by.items():
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
+                probe.probe_sleep(LEAD_US, stream)
                 e0.record(stream)
                 t0 = time.perf_counter()
                 graph.replay()
@@ -224,8 +228,6 @@ def time_read_probe(w: dict, views, path: str, splits: int, steps: int = 50,
     """Read-only probe over the pages of one plan's tasks (libpkv_probe.so):
     the HBM rate of the split kernel's access pattern with no compute.
     Returns the median µs per probe launch and the real-KV GB/s it implies."""
-    from . import probe
-
     prob = engine.problem_from_workload(w, "auto")
     step = engine.DecodeStep(prob, path, splits)
     stream = torch.cuda.current_stream()
@@ -238,6 +240,7 @@ def time_read_probe(w: dict, views, path: str, splits: int, steps: int = 50,
     runs = []
     for rep in range(repeats):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        probe.probe_sleep(LEAD_US, stream)
         e0.record(stream)
         for i in range(steps):
             probe.probe_read(views[(warmup + rep * steps + i) % n], step, sink, stream)
@@ -289,6 +292,7 @@ def time_device_path(w: dict, views, splits: int, steps: int = 50, warmup: int =
     with torch.cuda.stream(stream):
         for rep in range(repeats):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            probe.probe_sleep(LEAD_US, stream)
             e0.record(stream)
             for i in range(steps):
                 one(warmup + rep * steps + i)

@@ -89,3 +89,24 @@ def test_stream_and_empty_probes():
     probe.probe_empty(32, 256, flag)
     torch.cuda.synchronize()
     assert flag.tolist() == [7, 7] and int(sink.abs().sum()) == 0
+
+
+def test_sleep_probe_holds_the_device():
+    """pkv_probe_sleep keeps the stream busy for about the requested time and
+    then ends; out-of-range durations are rejected on the host."""
+    from paged_kv_gqa_block_amd import probe
+
+    say("[probe] sleep")
+    s = torch.cuda.current_stream()
+    for us in (0, 100, 400):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        probe.probe_sleep(us, s)
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        assert 0.8 * us / 1e3 <= ms < us / 1e3 + 5.0, (us, ms)
+    with pytest.raises(RuntimeError):
+        probe.probe_sleep(-1)
+    with pytest.raises(RuntimeError):
+        probe.probe_sleep(60000)
