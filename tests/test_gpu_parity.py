@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from paged_kv_gqa_block_amd import engine, traces
-from paged_kv_gqa_block_amd._lib import PKV_PLAN_HEADER_WORDS  # noqa: F401
+from paged_kv_gqa_block_amd._lib import PKV_ESHAPE, PkvError
 from tests.parity import check_lse, check_out, oracle_out, say
 
 pytestmark = pytest.mark.gpu
@@ -23,10 +23,19 @@ KERNELS = ("valu", "mfma")
 def _applicable(kernel, d, group):
     """The matrix-core kernel covers d = 128 (any G <= 16); the vector-ALU
     kernel covers d = 64 and 128 with G <= 8."""
-    if kernel == "mfma" and d != 128:
-        pytest.skip("matrix-core kernel is d=128 only")
-    if kernel == "valu" and group > 8:
-        pytest.skip("vector-ALU kernel is G<=8 only")
+    return not ((kernel == "mfma" and d != 128) or (kernel == "valu" and group > 8))
+
+
+def _check_rejected(w, path, splits, kernel):
+    """A split kernel asked for a shape it does not cover: the decode call
+    returns PKV_ESHAPE before any launch, and the stream stays usable."""
+    wd = engine.to_device(w)
+    step = engine.DecodeStep(engine.problem_from_workload(w, kernel), path, splits)
+    step.plan(wd["seq_lens_host"])
+    with pytest.raises(PkvError) as e:
+        step.decode(wd)
+    assert e.value.status == PKV_ESHAPE
+    torch.cuda.synchronize()
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -49,8 +58,11 @@ def _run(w, path, splits, kernel):
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("path", PATHS)
 def test_tiny_config_all_paths(path, kernel):
-    _applicable(kernel, 64, 4)
     w = traces.generate(traces.get_spec("tiny"), SEED)
+    if not _applicable(kernel, 64, 4):
+        say(f"[tiny] path={path} kernel={kernel}: rejected shape")
+        _check_rejected(w, path, w["spec"].splits, kernel)
+        return
     say(f"[tiny] path={path} kernel={kernel}")
     ref_out, ref_lse = oracle_out(w)
     step, _ = _run(w, path, w["spec"].splits, kernel)
@@ -154,9 +166,13 @@ EDGE_LENS = np.array([0, 1, 15, 16, 17, 33, 100, 0, 250], dtype=np.int32)
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (6, 2), (12, 2), (32, 2)])
 @pytest.mark.parametrize("dtype", ("f16", "bf16"))
 def test_edge_lengths_shapes_and_dtypes(d, hq, hkv, dtype, kernel):
-    _applicable(kernel, d, hq // hkv)
     spec = traces.custom_spec(len(EDGE_LENS), hq, hkv, d, splits=3, dtype=dtype)
     w = traces.generate(spec, SEED, seq_lens=EDGE_LENS)
+    if not _applicable(kernel, d, hq // hkv):
+        say(f"[edge] d={d} hq={hq} hkv={hkv} {dtype} kernel={kernel}: rejected shape")
+        for path, s in (("workqueue", 3), ("bucketed", 3), ("nosplit", 1), ("padded", 3)):
+            _check_rejected(w, path, s, kernel)
+        return
     say(f"[edge] d={d} hq={hq} hkv={hkv} {dtype} kernel={kernel}")
     ref_out, ref_lse = oracle_out(w)
     for path, s in (("workqueue", 3), ("workqueue", 40), ("bucketed", 3), ("bucketed", 40),
