@@ -41,14 +41,13 @@ METRIC = "decode-attention µs/step and achieved HBM GB/s (% of peak), paged GQA
 HBM_PEAK_GBS = 8000.0
 # Counter-based HBM traffic of the split kernel per workload (rocprofv3
 # FETCH_SIZE + WRITE_SIZE runs, scaled against a copy kernel); reported only
-# while the kernel sources still hash to the value recorded with it.
+# while the device sources (every file under csrc/) still hash to the value
+# recorded with it.
 TRAFFIC_PROFILES = {"long": "profiles/split_mfma_long_b1_n32768_traffic.txt",
                     "bimodal": "profiles/split_mfma_bimodal_b8_traffic.txt",
                     "zipf": "profiles/split_mfma_zipf_b8_traffic.txt",
                     "uniform": "profiles/split_mfma_uniform_b8_traffic.txt",
                     "policy_b64": "profiles/split_mfma_policy_b64_traffic.txt"}
-KERNEL_SOURCES = ("split_mfma.hip", "split_common.h", "device_common.h", "pkv_internal.h",
-                  "lens_plan.h")
 DEFAULT_PATH = {"tiny": "workqueue", "long": "bucketed", "bimodal": "workqueue",
                 "zipf": "workqueue", "uniform": "workqueue"}
 
@@ -89,12 +88,18 @@ def describe(spec, path, splits, lens):
 
 
 def kernel_source_hash() -> str:
+    """First 16 hex digits of the sha256 over every file under csrc/, in name
+    order, each as its name followed by its bytes."""
     import hashlib
 
+    csrc = os.path.join(ROOT, "paged_kv_gqa_block_amd", "csrc")
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_gqa_block_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(csrc)):
+        path = os.path.join(csrc, name)
+        if os.path.isfile(path):
+            h.update(name.encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
