@@ -25,7 +25,9 @@ measured time), with a small ridge term.  It also reports how the model's
 choices compare with the measured best, in sample, under 5-fold
 cross-validation over cells, leaving one batch size out and leaving one head
 shape out.  `measure` times the same candidates on the same (B, N_max) grid
-and seed for another head shape, head size or dtype and stores them beside
+and seed for another head shape, head size or dtype, with the table
+calibration's protocol (interleaved repeats of at least 2 ms of device time,
+on several placements of the buffers), and stores them beside
 the table (cost_calib_*.json); `fit` uses every such file too.  `check` measures, on
 held-out seed 20260623, the model's choice beside the table's choice and the
 four single paths, with interleaved repeats: on the two sweep families and on
@@ -47,7 +49,8 @@ import time
 import numpy as np
 
 from . import _lib, engine, traces
-from .calibrate import CANDIDATES, FAMILIES, NOISE, SINGLE_PATHS, cell_spec, grid_of, log, measure
+from .calibrate import (ALLOCATIONS, CANDIDATES, FAMILIES, NOISE, SINGLE_PATHS, cell_spec, grid_of,
+                        log, measure, time_cell)
 
 PATHS = ("bucketed", "workqueue", "nosplit", "padded")
 RIDGE = 1e-3
@@ -199,15 +202,18 @@ def cmd_measure(args) -> int:
     for b in traces.POLICY_BATCHES:
         for n in grid_of(b):
             n_max, times = measure(cell_spec(b, n, args.hq, args.hkv, args.dtype, args.d),
-                                   args.seed, CANDIDATES, args.steps, args.warmup)
+                                   args.seed, CANDIDATES, args.steps, args.warmup,
+                                   args.repeats, args.allocations)
             calib[f"{b}:{n}"] = {"batch": b, "cap": n, "n_max": n_max, "times": times}
+        log(f"  B={b}: {len(grid_of(b))} cells timed ({time.time() - t0:.0f} s so far)")
     held_out = args.seed != traces.CALIBRATION_SEED
     doc = {"about": ("Held-out timings of every candidate path on the (B, N_max) grid for one "
                      "head shape, used to check the cost model (not to fit it)." if held_out else
                      "Calibration timings of every candidate path on the (B, N_max) grid for "
                      "one head shape, used to fit the cost model."),
            "shape": shape, "calibration_seed": args.seed,
-           "device": torch.cuda.get_device_name(0), "calibration": calib,
+           "device": torch.cuda.get_device_name(0), "repeats": args.repeats,
+           "allocations": args.allocations, "calibration": calib,
            "seconds": round(time.time() - t0, 1)}
     stem = (f"hq{args.hq}_hkv{args.hkv}_{args.dtype}" + (f"_d{args.d}" if args.d != 128 else ""))
     name = f"cost_heldout_{stem}.json" if held_out else f"cost_calib_{stem}.json"
@@ -254,8 +260,6 @@ def cmd_fit(args) -> int:
 def cmd_check(args) -> int:
     import torch
 
-    from . import timing
-
     assert torch.cuda.is_available(), "the held-out check needs a GPU"
     with open(args.out) as f:
         doc = json.load(f)
@@ -275,11 +279,8 @@ def cmd_check(args) -> int:
             m_path, m_s, pred = engine.choose_model(model, sweep_problem(b), lens)
             t_path, t_s = engine.choose(rules, b, int(lens.max()))
             configs = list(dict.fromkeys(list(SINGLE_PATHS) + [(t_path, t_s), (m_path, m_s)]))
-            wd = engine.to_device(w)
-            engine.validate_inputs(wd)
-            views = timing.pool_copies(wd, 1.0, max_copies=8)
-            times = timing.time_paths_interleaved(w, views, configs, "auto", args.steps,
-                                                  args.warmup, repeats=7)
+            times, _, _, _ = time_cell(w, configs, args.steps, args.warmup, args.repeats,
+                                       args.allocations)
             t_model, t_table = times[f"{m_path}:{m_s}"], times[f"{t_path}:{t_s}"]
             best_single = min(times[f"{p}:{s}"] for p, s in SINGLE_PATHS)
             totals["model"] += t_model
@@ -294,8 +295,6 @@ def cmd_check(args) -> int:
                 "table_over_best_single": round(t_table / best_single, 4)}
             log(f"  {spec.name}: model {m_path}:{m_s} {t_model:.2f} us (predicted {pred:.2f}), "
                 f"table {t_path}:{t_s} {t_table:.2f} us, best single {best_single:.2f} us")
-            del views, wd, w
-            torch.cuda.empty_cache()
     held["traces"] = {}
     for name in TRACE_WORKLOADS:
         spec = traces.get_spec(name)
@@ -305,11 +304,8 @@ def cmd_check(args) -> int:
         t_path, t_s = engine.choose(rules, spec.batch, int(lens.max()))
         singles = [(p, (1 if p == "nosplit" else spec.splits)) for p, _ in SINGLE_PATHS]
         configs = list(dict.fromkeys(singles + [(t_path, t_s), (m_path, m_s)]))
-        wd = engine.to_device(w)
-        engine.validate_inputs(wd)
-        views = timing.pool_copies(wd, 1.0, max_copies=8)
-        times = timing.time_paths_interleaved(w, views, configs, "auto", args.steps,
-                                              args.warmup, repeats=7)
+        times, _, _, _ = time_cell(w, configs, args.steps, args.warmup, args.repeats,
+                                   args.allocations)
         t_model, t_table = times[f"{m_path}:{m_s}"], times[f"{t_path}:{t_s}"]
         best_single = min(times[f"{p}:{s}"] for p, s in singles)
         held["traces"][name] = {
@@ -320,9 +316,8 @@ def cmd_check(args) -> int:
             "table_over_best_single": round(t_table / best_single, 4)}
         log(f"  {name}: model {m_path}:{m_s} {t_model:.2f} us (predicted {pred:.2f}), "
             f"table {t_path}:{t_s} {t_table:.2f} us, best single {best_single:.2f} us")
-        del views, wd, w
-        torch.cuda.empty_cache()
     doc["heldout"] = {"seed": traces.HELD_OUT_SEED, "device": torch.cuda.get_device_name(0),
+                      "repeats": args.repeats, "allocations": args.allocations,
                       "cells": held, "total_us": {k: round(v, 2) for k, v in totals.items()},
                       "seconds": round(time.time() - t0, 1)}
     with open(args.out, "w") as f:
@@ -389,6 +384,10 @@ def main(argv=None) -> int:
     ap.add_argument("--out", default=engine.COST_MODEL_PATH)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--repeats", type=int, default=7,
+                    help="measure, check: interleaved timed repeats per placement")
+    ap.add_argument("--allocations", type=int, default=ALLOCATIONS,
+                    help="measure, check: placements of each cell's buffers in memory")
     args = ap.parse_args(argv)
     return {"measure": cmd_measure, "fit": cmd_fit, "check": cmd_check,
             "evaluate": cmd_evaluate}[args.cmd](args)
