@@ -401,9 +401,13 @@ pkv_status pkv_policy(const pkv_policy_table* table, int32_t batch, int32_t max_
 /*
  * Default path choice of the engine: for B = 1 the calibrated table's rule
  * for (1, N_1) (pkv_policy: the one row's length fixes the workload); for
- * B >= 2 the learned cost model's choice among its candidates
- * (pkv_policy_model), because with several rows the length mix, not only
- * (B, N_max), decides how evenly the split launch loads the CUs.  The pages
+ * B >= 2 the learned cost model's choice (the smallest prediction, as
+ * pkv_policy_model) among its candidates and the CU-balanced workqueue caps
+ * (pkv_balanced_splits with per_cu = 1 and 2, bounded by the largest
+ * WORKQUEUE split cap among the candidates; a cap already listed, or 0, is
+ * not added, and on equal predictions the listed candidate wins), because
+ * with several rows the length mix, not only (B, N_max), decides how evenly
+ * the split launch loads the CUs.  The pages
  * calibrate thresholds on (B, N_max) ("Metodologia / 2. Politica Adaptativa
  * Calibrada", es page) and name a learned cost model as the next step
  * ("Significado y Reivindicaciones" / "Direcciones Futuras"); this policy
@@ -416,6 +420,23 @@ pkv_status pkv_policy(const pkv_policy_table* table, int32_t batch, int32_t max_
 pkv_status pkv_policy_default(const pkv_policy_table* table, const pkv_cost_model* model,
                               const pkv_problem* prob, const int32_t* seq_lens_host,
                               int32_t* scratch_host, int32_t* path_out, int32_t* splits_out);
+
+/*
+ * CU-balanced split cap of the compact workqueue: the largest S in
+ * [1, max_splits] whose WORKQUEUE plan (pkv_plan's task count, Hkv * sum_i
+ * ceil(T_i / ceil(T_max / S))) holds at most per_cu * num_cus tasks, so that
+ * one launch deals every CU at most about per_cu tasks of near-equal size;
+ * *splits_out = 0 when even S = 1 holds more.  The split rule of the pages
+ * ("Row-local bounds", "Compact workqueue") is unchanged: S, the split cap
+ * a policy chooses, only sets the granule, and the default policy scores
+ * this cap beside its listed candidates.  Host only, O(B log max_splits).
+ * num_cus 1..1024, per_cu 1..64, max_splits 1..65535.  Errors: PKV_EINVAL
+ * (null pointer, an argument out of range), PKV_ESHAPE, PKV_EDTYPE,
+ * PKV_ERANGE (a length outside [0, max_pages_per_row * P]).
+ */
+pkv_status pkv_balanced_splits(const pkv_problem* prob, const int32_t* seq_lens_host,
+                               int32_t num_cus, int32_t per_cu, int32_t max_splits,
+                               int32_t* splits_out);
 
 /*
  * Decode step that allocates nothing, for callers that cannot allocate

@@ -43,6 +43,7 @@ EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pk
             "pkv_plan_device", "pkv_decode_device", "pkv_merge_device", "pkv_decode_selfplan",
             "pkv_merge_selfplan", "pkv_append_kv",
             "pkv_policy", "pkv_cost_features", "pkv_policy_model", "pkv_policy_default",
+            "pkv_balanced_splits",
             "pkv_noalloc_bytes", "pkv_attend_noalloc", "pkv_status_str")
 PKV_COST_FEATURES = 7
 
@@ -140,6 +141,8 @@ def _load() -> ctypes.CDLL:
                                        ctypes.POINTER(pkv_cost_model), prob_p, vp, vp,
                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.pkv_policy_default.restype = i32
+    lib.pkv_balanced_splits.argtypes = [prob_p, vp, i32, i32, i32, ctypes.POINTER(i32)]
+    lib.pkv_balanced_splits.restype = i32
     lib.pkv_noalloc_bytes.argtypes = [prob_p, i32]
     lib.pkv_noalloc_bytes.restype = ctypes.c_size_t
     lib.pkv_attend_noalloc.argtypes = [prob_p, vp, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -383,6 +386,16 @@ def pkv_policy_default(rules, prob: pkv_problem, candidates, weights, num_cus: i
         ctypes.byref(table), ctypes.byref(model), ctypes.byref(prob), lens.ctypes.data,
         scratch.ctypes.data, ctypes.byref(path), ctypes.byref(splits)))
     return path.value, splits.value
+
+
+def pkv_balanced_splits(prob: pkv_problem, seq_lens_host, num_cus: int, per_cu: int,
+                        max_splits: int) -> int:
+    """The CU-balanced workqueue split cap (0 when none fits the budget)."""
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    out = ctypes.c_int32()
+    _check("pkv_balanced_splits", LIB.pkv_balanced_splits(
+        ctypes.byref(prob), lens.ctypes.data, num_cus, per_cu, max_splits, ctypes.byref(out)))
+    return out.value
 
 
 def decode_plan(plan_host) -> dict:

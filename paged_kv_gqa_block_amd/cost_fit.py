@@ -179,16 +179,38 @@ def cross_validate(samples) -> dict:
     return res
 
 
+SWEEP_SHAPE = {"num_q_heads": 64, "num_kv_heads": 8, "dtype": "bf16", "head_dim": 128}
+
+
 def all_samples(table_path: str):
+    """Every calibration timing: the cost_calib_*.json files, and the policy
+    table's own timings unless one of those files covers the table's sweep
+    shape (then the table's cells would be counted twice)."""
     with open(table_path) as f:
         table = json.load(f)
-    samples, sources = samples_from_table(table), ["policy_table.json"]
+    extras = []
     for path in sorted(glob.glob(EXTRA_GLOB)):
         with open(path) as f:
-            extra = json.load(f)
-        samples += samples_from_table(extra, extra["shape"])
-        sources.append(os.path.basename(path))
+            extras.append((os.path.basename(path), json.load(f)))
+    samples, sources = [], []
+    if not any(doc["shape"] == SWEEP_SHAPE for _, doc in extras):
+        samples, sources = samples_from_table(table), ["policy_table.json"]
+    for name, doc in extras:
+        samples += samples_from_table(doc, doc["shape"])
+        sources.append(name)
     return table, samples, sources
+
+
+def balanced_candidates(prob, lens):
+    """The CU-balanced workqueue caps that the default policy adds to the
+    model's candidates (pkv_policy_default), when not among them."""
+    caps = [s for p, s in CANDIDATES if p == "workqueue"]
+    out = []
+    for per_cu in (1, 2):
+        s = _lib.pkv_balanced_splits(prob, lens, NUM_CUS, per_cu, max(caps))
+        if s > 0 and ("workqueue", s) not in list(CANDIDATES) + out:
+            out.append(("workqueue", s))
+    return out
 
 
 def cmd_measure(args) -> int:
@@ -201,8 +223,10 @@ def cmd_measure(args) -> int:
     t0 = time.time()
     for b in traces.POLICY_BATCHES:
         for n in grid_of(b):
-            n_max, times = measure(cell_spec(b, n, args.hq, args.hkv, args.dtype, args.d),
-                                   args.seed, CANDIDATES, args.steps, args.warmup,
+            spec = cell_spec(b, n, args.hq, args.hkv, args.dtype, args.d)
+            lens = traces.draw_lengths(spec, np.random.default_rng(args.seed))
+            configs = list(CANDIDATES) + balanced_candidates(sweep_problem(b, shape), lens)
+            n_max, times = measure(spec, args.seed, configs, args.steps, args.warmup,
                                    args.repeats, args.allocations)
             calib[f"{b}:{n}"] = {"batch": b, "cap": n, "n_max": n_max, "times": times}
         log(f"  B={b}: {len(grid_of(b))} cells timed ({time.time() - t0:.0f} s so far)")
@@ -327,15 +351,17 @@ def cmd_check(args) -> int:
 
 
 def evaluate_file(path: str, model_path: str) -> dict:
-    """The model's and the table's choices against the best candidate and the
-    best single path, on the stored timings of one file (any shape, any seed)."""
+    """The model's, the table's and the default policy's choices against the
+    best candidate and the best single path, on the stored timings of one
+    file (any shape, any seed)."""
     with open(path) as f:
         doc = json.load(f)
     shape = doc["shape"]
     model = engine.load_cost_model(model_path)
     rules = engine.load_policy_table()
-    tot = {"model": 0.0, "table": 0.0, "best": 0.0, **{f"{p}:{s}": 0.0 for p, s in SINGLE_PATHS}}
-    worse = {"model": 0, "table": 0}
+    tot = {"model": 0.0, "table": 0.0, "default": 0.0, "best": 0.0,
+           **{f"{p}:{s}": 0.0 for p, s in SINGLE_PATHS}}
+    worse = {"model": 0, "table": 0, "default": 0}
     for cell in doc["calibration"].values():
         b, cap, times = cell["batch"], cell["cap"], cell["times"]
         lens = traces.draw_lengths(cell_spec(b, cap), np.random.default_rng(doc["calibration_seed"]))
@@ -343,8 +369,10 @@ def evaluate_file(path: str, model_path: str) -> dict:
             raise RuntimeError(f"{path}: regenerated lengths differ from the measured ones")
         m_path, m_s, _ = engine.choose_model(model, sweep_problem(b, shape), lens)
         t_path, t_s = engine.choose(rules, b, int(lens.max()))
+        d_path, d_s = engine.choose_default(rules, model, sweep_problem(b, shape), lens)
         best = min(times.values())
-        for who, key in (("model", f"{m_path}:{m_s}"), ("table", f"{t_path}:{t_s}")):
+        for who, key in (("model", f"{m_path}:{m_s}"), ("table", f"{t_path}:{t_s}"),
+                         ("default", f"{d_path}:{d_s}")):
             tot[who] += times[key]
             worse[who] += times[key] > best * (1 + NOISE)
         tot["best"] += best
@@ -355,6 +383,7 @@ def evaluate_file(path: str, model_path: str) -> dict:
             "total_us": {k: round(v, 2) for k, v in tot.items()},
             "model_over_best": round(tot["model"] / tot["best"] - 1, 4),
             "table_over_best": round(tot["table"] / tot["best"] - 1, 4),
+            "default_over_best": round(tot["default"] / tot["best"] - 1, 4),
             "cells_over_3pct": worse}
 
 

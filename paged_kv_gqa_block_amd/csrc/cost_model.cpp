@@ -16,6 +16,9 @@ using namespace pkv;
 namespace {
 
 constexpr int kMaxCus = 1024;
+// Tasks per CU of the balanced workqueue candidates of pkv_policy_default.
+constexpr int32_t kNumBalanced = 2;
+constexpr int32_t kBalancedPerCu[kNumBalanced] = {1, 2};
 
 // Per-CU load of one launch: grid item j goes to CU j mod num_cus (the
 // round-robin spread of a launch's workgroups); max() is the largest sum of
@@ -141,7 +144,54 @@ pkv_status features(const pkv_problem* prob, const int32_t* lens, int32_t path, 
 
 bool valid_cus(int32_t n) { return n >= 1 && n <= kMaxCus; }
 
+// Largest split cap S in [1, max_splits] whose compact workqueue holds at
+// most per_cu * num_cus tasks, or 0 when even S = 1 holds more.  The task
+// count of S (count_plan: Hkv * sum_i ceil(T_i / ceil(T_max / S))) never
+// decreases as S grows, so the cap is found by bisection.  Lengths must be
+// valid.
+int32_t balanced_splits(const pkv_problem& p, const int32_t* lens, int32_t num_cus,
+                        int32_t per_cu, int32_t max_splits) {
+  const int64_t budget = int64_t(per_cu) * num_cus;
+  auto tasks = [&](int32_t s) { return count_plan(p, lens, PKV_WORKQUEUE, s, nullptr).n_tasks; };
+  if (tasks(1) > budget) return 0;
+  int32_t lo = 1, hi = max_splits;  // tasks(lo) <= budget
+  while (lo < hi) {
+    const int32_t mid = lo + (hi - lo + 1) / 2;
+    if (tasks(mid) <= budget) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The model's step time of candidate (path, s) in microseconds.
+pkv_status predict(const pkv_problem* prob, const pkv_cost_model* model, const int32_t* lens,
+                   int32_t path, int32_t s, int32_t* scratch, double* y) {
+  float f[PKV_COST_FEATURES];
+  const pkv_status st = features(prob, lens, path, path == PKV_NOSPLIT ? 1 : s, model->num_cus,
+                                 scratch, f);
+  if (st != PKV_OK) return st;
+  const float* w = model->weights + PKV_COST_FEATURES * path;
+  *y = 0.0;
+  for (int j = 0; j < PKV_COST_FEATURES; ++j) *y += double(w[j]) * f[j];
+  return PKV_OK;
+}
+
 }  // namespace
+
+extern "C" pkv_status pkv_balanced_splits(const pkv_problem* prob, const int32_t* seq_lens_host,
+                                          int32_t num_cus, int32_t per_cu, int32_t max_splits,
+                                          int32_t* splits_out) {
+  pkv_status st = check_problem(prob);
+  if (st != PKV_OK) return st;
+  if (!seq_lens_host || !splits_out) return PKV_EINVAL;
+  if (!valid_cus(num_cus) || per_cu < 1 || per_cu > 64 || max_splits < 1 || max_splits > 65535)
+    return PKV_EINVAL;
+  const int64_t cap = int64_t(prob->max_pages_per_row) * prob->page_size;
+  for (int32_t i = 0; i < prob->batch; ++i)
+    if (seq_lens_host[i] < 0 || seq_lens_host[i] > cap) return PKV_ERANGE;
+  *splits_out = balanced_splits(*prob, seq_lens_host, num_cus, per_cu, max_splits);
+  return PKV_OK;
+}
 
 extern "C" pkv_status pkv_cost_features(const pkv_problem* prob, const int32_t* seq_lens_host,
                                         int32_t path, int32_t max_splits, int32_t num_cus,
@@ -170,23 +220,17 @@ extern "C" pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_m
     if (path < PKV_BUCKETED || path > PKV_PADDED || s < 1 || s > 65535) return PKV_EINVAL;
   }
   double best = INFINITY;
-  int32_t best_k = 0;
-  float f[PKV_COST_FEATURES];
   for (int32_t k = 0; k < model->n_candidates; ++k) {
     const int32_t path = model->candidates[2 * k], s = model->candidates[2 * k + 1];
-    st = features(prob, seq_lens_host, path, path == PKV_NOSPLIT ? 1 : s, model->num_cus,
-                  scratch_host, f);
-    if (st != PKV_OK) return st;
-    const float* w = model->weights + PKV_COST_FEATURES * path;
     double y = 0.0;
-    for (int j = 0; j < PKV_COST_FEATURES; ++j) y += double(w[j]) * f[j];
+    st = predict(prob, model, seq_lens_host, path, s, scratch_host, &y);
+    if (st != PKV_OK) return st;
     if (y < best) {  // the first candidate wins a tie
       best = y;
-      best_k = k;
+      *path_out = path;
+      *splits_out = s;
     }
   }
-  *path_out = model->candidates[2 * best_k];
-  *splits_out = model->candidates[2 * best_k + 1];
   if (predicted_us_out) *predicted_us_out = float(best);
   return PKV_OK;
 }
@@ -208,6 +252,50 @@ extern "C" pkv_status pkv_policy_default(const pkv_policy_table* table,
   // workload.  Several rows: the length mix decides the load balance, which
   // the model's per-CU feature sees and the table's key does not.
   if (prob->batch == 1) return pkv_policy(table, 1, n_max, path_out, splits_out);
-  return pkv_policy_model(prob, model, seq_lens_host, scratch_host, path_out, splits_out,
-                          nullptr);
+  // The model's candidates, then the CU-balanced workqueue caps
+  // (kBalancedPerCu tasks per CU, at most the model's largest workqueue cap)
+  // that are not among them; the first of equal predictions wins.
+  if (model->n_candidates < 1 || !model->candidates || !model->weights ||
+      !valid_cus(model->num_cus))
+    return PKV_EINVAL;
+  int32_t s_max = 0;
+  for (int32_t k = 0; k < model->n_candidates; ++k) {
+    const int32_t path = model->candidates[2 * k], s = model->candidates[2 * k + 1];
+    if (path < PKV_BUCKETED || path > PKV_PADDED || s < 1 || s > 65535) return PKV_EINVAL;
+    if (path == PKV_WORKQUEUE) s_max = std::max(s_max, s);
+  }
+  double best = INFINITY;
+  for (int32_t k = 0; k < model->n_candidates; ++k) {
+    const int32_t path = model->candidates[2 * k], s = model->candidates[2 * k + 1];
+    double y = 0.0;
+    st = predict(prob, model, seq_lens_host, path, s, scratch_host, &y);
+    if (st != PKV_OK) return st;
+    if (y < best) {
+      best = y;
+      *path_out = path;
+      *splits_out = s;
+    }
+  }
+  int32_t bal[kNumBalanced];
+  for (int32_t i = 0; i < kNumBalanced; ++i)
+    bal[i] = s_max > 0 ? balanced_splits(*prob, seq_lens_host, model->num_cus,
+                                         kBalancedPerCu[i], s_max)
+                       : 0;
+  for (int32_t i = 0; i < kNumBalanced; ++i) {
+    const int32_t s = bal[i];
+    bool listed = (s == 0);  // 0: no cap keeps the tasks within the budget
+    for (int32_t k = 0; k < model->n_candidates; ++k)
+      listed |= model->candidates[2 * k] == PKV_WORKQUEUE && model->candidates[2 * k + 1] == s;
+    for (int32_t j = 0; j < i; ++j) listed |= bal[j] == s;
+    if (listed) continue;
+    double y = 0.0;
+    st = predict(prob, model, seq_lens_host, PKV_WORKQUEUE, s, scratch_host, &y);
+    if (st != PKV_OK) return st;
+    if (y < best) {
+      best = y;
+      *path_out = PKV_WORKQUEUE;
+      *splits_out = s;
+    }
+  }
+  return PKV_OK;
 }

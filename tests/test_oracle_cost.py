@@ -185,6 +185,75 @@ def test_default_policy_hand_worked():
     assert _lib.pkv_policy_default(crules, four, cands, w, 4, LENS) == (_lib.PKV_PADDED, 4)
 
 
+# Workqueue task counts of LENS (pages 19, 2, 19, 0) with Hkv = 2, by cap S:
+#   S=1: granule 19 -> 1 + 1 + 1 tasks per head -> 6;  S=2: granule 10 -> 2+1+2 -> 10;
+#   S=3: granule 7 -> 3+1+3 -> 14;  S=4: granule 5 -> 4+1+4 -> 18;  S=5: granule 4 -> 5+1+5 -> 22
+BALANCED_HAND = [  # (num_cus, per_cu, max_splits, cap)
+    (4, 1, 64, 0),   # budget 4 < 6 tasks at S = 1
+    (4, 2, 64, 1),   # budget 8
+    (4, 3, 64, 2),   # budget 12
+    (4, 5, 64, 4),   # budget 20: 18 <= 20 < 22
+    (4, 5, 3, 3),    # the same budget, capped at 3
+]
+
+
+def test_balanced_splits_hand_counted():
+    from oracle import policy
+
+    prob = _lib.make_problem(4, 4, 2, 64, 16, 4096, 64)
+    for cus, per_cu, smax, want in BALANCED_HAND:
+        assert policy.balanced_splits(LENS, 2, 4, 64, 16, cus, per_cu, smax) == want
+        assert _lib.pkv_balanced_splits(prob, LENS, cus, per_cu, smax) == want
+    for bad in ((0, 1, 4), (4, 0, 4), (4, 65, 4), (4, 1, 0)):
+        with pytest.raises(PkvError) as e:
+            _lib.pkv_balanced_splits(prob, LENS, *bad)
+        assert e.value.status == _lib.PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        _lib.pkv_balanced_splits(prob, [300, 17, 300, 64 * 16 + 1], 4, 1, 4)
+    assert e.value.status == _lib.PKV_ERANGE
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_c_balanced_splits_matches_oracle(seed):
+    from oracle import policy
+
+    rng = np.random.default_rng(1700 + seed)
+    for _ in range(6):
+        b = int(rng.integers(1, 24))
+        hkv = int(rng.choice([1, 2, 8]))
+        lens = rng.integers(0, 8192, size=b, endpoint=True)
+        lens[rng.random(b) < 0.2] = 0
+        prob = _lib.make_problem(b, hkv * 4, hkv, 128, 16, 1 << 20, 512)
+        cus, per_cu, smax = int(rng.choice([4, 64, 256])), int(rng.integers(1, 4)), 40
+        assert _lib.pkv_balanced_splits(prob, lens, cus, per_cu, smax) == \
+            policy.balanced_splits(lens, hkv, hkv * 4, 128, 16, cus, per_cu, smax)
+
+
+def test_default_policy_takes_a_balanced_cap():
+    """Weights that price the workqueue by its task count (1 µs per task) and
+    every other path at 1000 µs: among HAND_CANDS the workqueue at S = 4 (18
+    tasks) wins; the balanced cap for 2 tasks per CU on 4 CUs (S = 1, 6
+    tasks) is cheaper still, and the default policy takes it.  The balanced
+    cap for 1 task per CU does not exist (6 > 4 tasks at S = 1)."""
+    from oracle import policy
+
+    w = [[1000, 0, 0, 0, 0, 0, 0], [0, 0, 0, 0, 0, 0, 1000],
+         [1000, 0, 0, 0, 0, 0, 0], [1000, 0, 0, 0, 0, 0, 0]]
+    rules = [(1, 1 << 30, 0, 1 << 30, "nosplit", 1)]
+    assert cost.choose(w, HAND_CANDS, LENS, 2, 4, 64, 16, 4)[:2] == ("workqueue", 4)
+    assert policy.choose_default(rules, w, HAND_CANDS, LENS, 2, 4, 64, 16, 4) == \
+        ("workqueue", 1)
+    cands = [(_lib.PATH_IDS[p], s) for p, s in HAND_CANDS]
+    crules = [r[:4] + (_lib.PATH_IDS[r[4]], r[5]) for r in rules]
+    four = _lib.make_problem(4, 4, 2, 64, 16, 4096, 64)
+    assert _lib.pkv_policy_default(crules, four, cands, np.asarray(w, np.float32), 4, LENS) == \
+        (_lib.PKV_WORKQUEUE, 1)
+    # With the workqueue at S = 1 listed, the listed candidate is scored and
+    # the balanced cap adds nothing.
+    listed = HAND_CANDS + [("workqueue", 1)]
+    assert policy.choose_default(rules, w, listed, LENS, 2, 4, 64, 16, 4) == ("workqueue", 1)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_c_default_policy_matches_oracle(seed):
     from oracle import policy
@@ -208,7 +277,10 @@ def test_c_default_policy_matches_oracle(seed):
         if b == 1:
             assert (PATH_NAMES[got[0]], got[1]) == want
         else:  # the model's argmin; float32 (C) and float64 (oracle) may split a near tie
+            caps = [policy.balanced_splits(lens, 8, 64, 128, 16, cus, k, 64) for k in (1, 2)]
+            scored = ocands + [("workqueue", s) for s in caps if s > 0]
+            assert (PATH_NAMES[got[0]], got[1]) in scored
             ys = {c: cost.predict_us(w, c[0], cost.features(lens, 8, 64, 128, 16, c[1], c[0],
-                                                            cus)) for c in ocands}
+                                                            cus)) for c in scored}
             best = min(ys.values())
             assert ys[(PATH_NAMES[got[0]], got[1])] <= best + 1e-4 * max(1.0, abs(best))
