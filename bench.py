@@ -14,10 +14,11 @@ pools (as consecutive layers of a model would), with enough copies to exceed
 host enqueues a kernel in a few microseconds, well under the device time of
 these steps); with --launch graph they are captured once in a HIP graph,
 launched once untimed and then replayed.  The line also reports the same K
-steps launched the other way (on these device-bound steps graph replay is
-0-2 us per step slower, the short launch-bound steps of the policy sweep are
-where it pays).  For the long and bimodal workloads the line carries
-both target workloads' figures in `targets`.
+steps launched the other way (on these device-bound steps the two agree
+within about 1 us per step; the short launch-bound steps of the policy sweep
+are where graph replay pays).  For the long and bimodal workloads the line
+carries both target workloads' figures in `targets`, each with the step time
+of the engine's default policy (its own path and split cap) beside it.
 
 Printed JSON line: value = real-KV bytes (sum N_i * Hkv * d * 2 * 2) divided by
 the device step time measured with HIP events on the launch stream.  The
@@ -422,6 +423,18 @@ def main(argv=None):
                              "split_roofline": {k: t["roofline"][k] for k in
                                                 ("achieved", "frac", "launch_us", "traffic")},
                              "read_only_probe": t["roofline"].get("read_only_probe")}
+            # The engine's default policy on the same workload (its own path
+            # and split cap), timed the same way.
+            lens_t = w["seq_lens"].numpy()
+            dpath, ds = engine.choose_default(engine.load_policy_table(),
+                                              engine.load_cost_model(),
+                                              engine.problem_from_workload(w), lens_t)
+            tconf = (t["config"]["path"], t["config"]["splits"])
+            d = t if (dpath, ds) == tconf else measure(args, w, wd, dpath, ds, seed,
+                                                       with_probe=False)
+            targets[name]["default_policy"] = {
+                "path": dpath, "splits": ds, "us_per_step": d["us_per_step"], "GB/s": d["GB/s"],
+                "pct_of_peak": d["pct_of_peak"]}
         line["targets"] = targets
         w = traces.generate(spec, seed)  # the contract workload again, for the CPU leg
     if not args.no_cpu_baseline:
