@@ -248,8 +248,9 @@ def check_default(out_path: str, steps: int, warmup: int, repeats: int,
     ok_all, sums_ok, totals = summarise(record)
     doc = {
         "about": "Held-out check of the default policy (pkv_policy_default: calibrated table "
-                 "for B = 1, learned cost model over workqueue and no-split candidates for "
-                 "B >= 2) against the four fixed single paths.",
+                 "for B = 1, learned cost model over the workqueue and no-split candidates "
+                 "and the CU-balanced workqueue caps for B >= 2) against the four fixed "
+                 "single paths.",
         "heldout_seed": traces.HELD_OUT_SEED,
         "device": torch.cuda.get_device_name(0),
         "repeats": repeats, "allocations": allocations, "min_band": MIN_BAND,
@@ -276,7 +277,8 @@ def main(argv=None):
                          "and rerun only the held-out check")
     ap.add_argument("--check-default", action="store_true",
                     help="only run the held-out check of the default policy (table for "
-                         "B = 1, cost model for B >= 2) and write policy_heldout.json")
+                         "B = 1, cost model with the balanced caps for B >= 2) and write "
+                         "policy_heldout.json")
     ap.add_argument("--repeats", type=int, default=7,
                     help="timed repeats per placement")
     ap.add_argument("--allocations", type=int, default=ALLOCATIONS,

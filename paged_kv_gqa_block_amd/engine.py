@@ -236,7 +236,8 @@ DEFAULT_MODEL_PATHS = (PKV_WORKQUEUE, PKV_NOSPLIT)
 def choose_default(rules, model, prob: _lib.pkv_problem, seq_lens_host):
     """Path name and split cap of the engine's default policy
     (pkv_policy_default): the calibrated table for one row, the learned cost
-    model (workqueue and no-split candidates) for several."""
+    model (workqueue and no-split candidates, and the CU-balanced workqueue
+    caps the library adds) for several."""
     cands, weights, num_cus = model
     cands = [c for c in cands if c[0] in DEFAULT_MODEL_PATHS]
     path, splits = _lib.pkv_policy_default(rules, prob, cands, weights[split_kernel_of(prob)],

@@ -106,7 +106,8 @@ def test_rules_use_known_paths():
 
 
 def test_recorded_default_policy_heldout_check():
-    """The engine's default policy (table for B = 1, cost model for B >= 2) on
+    """The engine's default policy (table for B = 1, cost model with the
+    CU-balanced workqueue caps for B >= 2) on
     the held-out seed, recorded by `calibrate --check-default`: every cell
     (both sweep families at every batch size, and the long, bimodal, zipf,
     uniform and tiny workloads) within its measured noise band of the best
