@@ -444,6 +444,25 @@ def test_cost_model_choice_matches_oracle(name):
     check_lse(step.lse, ref_lse, rows=rows, label=f"model/{name}/{path}:{s}")
 
 
+@pytest.mark.parametrize("name", ("bimodal", "zipf", "uniform", "policy_b4", "policy_b8",
+                                  "policy_short_b8", "policy_short_b16"))
+def test_default_policy_choice_matches_oracle(name):
+    """The engine's default choice (pkv_policy_default), which on these
+    workloads is the workqueue at a CU-balanced split cap outside the listed
+    8/16/32/64 (e.g. 15 on bimodal, 3 on the short B = 16 sweep), run through
+    the C ABI against the oracle."""
+    w = traces.generate(traces.get_spec(name), SEED)
+    spec = w["spec"]
+    lens = w["seq_lens"].numpy()
+    path, s = engine.choose_default(engine.load_policy_table(), engine.load_cost_model(),
+                                    engine.problem_from_workload(w), lens)
+    say(f"[default policy {name}] choice {path}:{s}")
+    ref_out, ref_lse = oracle_out(w)
+    step, _ = _run(w, path, s, "auto")
+    check_out(step.out, ref_out, spec.dtype, label=f"default/{name}/{path}:{s}")
+    check_lse(step.lse, ref_lse, label=f"default/{name}/{path}:{s}")
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_nosplit_takes_row_lengths_from_the_plan(kernel):
     """pkv_decode reads every row's length from the plan on every path: on the
