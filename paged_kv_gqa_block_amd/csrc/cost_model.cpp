@@ -220,6 +220,7 @@ extern "C" pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_m
     if (path < PKV_BUCKETED || path > PKV_PADDED || s < 1 || s > 65535) return PKV_EINVAL;
   }
   double best = INFINITY;
+  int32_t best_path = 0, best_s = 0;
   for (int32_t k = 0; k < model->n_candidates; ++k) {
     const int32_t path = model->candidates[2 * k], s = model->candidates[2 * k + 1];
     double y = 0.0;
@@ -227,10 +228,12 @@ extern "C" pkv_status pkv_policy_model(const pkv_problem* prob, const pkv_cost_m
     if (st != PKV_OK) return st;
     if (y < best) {  // the first candidate wins a tie
       best = y;
-      *path_out = path;
-      *splits_out = s;
+      best_path = path;
+      best_s = s;
     }
   }
+  *path_out = best_path;
+  *splits_out = best_s;
   if (predicted_us_out) *predicted_us_out = float(best);
   return PKV_OK;
 }
@@ -265,6 +268,7 @@ extern "C" pkv_status pkv_policy_default(const pkv_policy_table* table,
     if (path == PKV_WORKQUEUE) s_max = std::max(s_max, s);
   }
   double best = INFINITY;
+  int32_t best_path = 0, best_s = 0;
   for (int32_t k = 0; k < model->n_candidates; ++k) {
     const int32_t path = model->candidates[2 * k], s = model->candidates[2 * k + 1];
     double y = 0.0;
@@ -272,8 +276,8 @@ extern "C" pkv_status pkv_policy_default(const pkv_policy_table* table,
     if (st != PKV_OK) return st;
     if (y < best) {
       best = y;
-      *path_out = path;
-      *splits_out = s;
+      best_path = path;
+      best_s = s;
     }
   }
   int32_t bal[kNumBalanced];
@@ -293,9 +297,11 @@ extern "C" pkv_status pkv_policy_default(const pkv_policy_table* table,
     if (st != PKV_OK) return st;
     if (y < best) {
       best = y;
-      *path_out = PKV_WORKQUEUE;
-      *splits_out = s;
+      best_path = PKV_WORKQUEUE;
+      best_s = s;
     }
   }
+  *path_out = best_path;
+  *splits_out = best_s;
   return PKV_OK;
 }
