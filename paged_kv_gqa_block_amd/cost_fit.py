@@ -100,13 +100,39 @@ def kernel_of(key: str) -> str:
 KERNELS = ("mfma", "mfma_g16", "valu")
 
 
+SKEWED = ("bimodal", "zipf")
+SKEWED_BATCHES = (2, 4, 8, 16, 32)
+
+
+def skewed_spec(dist: str, batch: int, shape: dict | None = None) -> traces.WorkloadSpec:
+    """A batch of `batch` rows with the bimodal or Zipf length mix of the
+    trace workloads, in the given head shape (the sweep's by default)."""
+    base = traces.get_spec(dist)
+    shape = shape or {}
+    sweep = traces.get_spec("policy_b8")
+    return traces.WorkloadSpec(f"cal_{dist}_b{batch}", batch,
+                               shape.get("num_q_heads", sweep.num_q_heads),
+                               shape.get("num_kv_heads", sweep.num_kv_heads),
+                               shape.get("head_dim", sweep.head_dim), base.page_size,
+                               base.lengths, base.splits, shape.get("dtype", sweep.dtype),
+                               lo=base.lo, hi=base.hi)
+
+
+def spec_of_cell(cell: dict, shape: dict | None = None) -> traces.WorkloadSpec:
+    """The workload a stored calibration cell timed: a sweep cell (batch,
+    longest length) or a skewed cell (batch, length mix)."""
+    if "dist" in cell:
+        return skewed_spec(cell["dist"], cell["batch"], shape)
+    return cell_spec(cell["batch"], cell["cap"])
+
+
 def samples_from_table(table: dict, shape: dict | None = None):
     """(cell, candidate, path, features, us) of every calibration timing."""
     out = []
     tag = shape_tag(shape)
     for key, cell in table["calibration"].items():
-        b, cap = cell["batch"], cell["cap"]
-        lens = traces.draw_lengths(cell_spec(b, cap),
+        b = cell["batch"]
+        lens = traces.draw_lengths(spec_of_cell(cell, shape),
                                    np.random.default_rng(table["calibration_seed"]))
         if int(lens.max()) != cell["n_max"]:
             raise RuntimeError(f"cell {key}: regenerated lengths differ from the measured ones")
@@ -221,7 +247,17 @@ def cmd_measure(args) -> int:
              "head_dim": args.d}
     calib = {}
     t0 = time.time()
-    for b in traces.POLICY_BATCHES:
+    if args.skewed:
+        for dist in SKEWED:
+            for b in SKEWED_BATCHES:
+                spec = skewed_spec(dist, b, shape)
+                lens = traces.draw_lengths(spec, np.random.default_rng(args.seed))
+                configs = list(CANDIDATES) + balanced_candidates(sweep_problem(b, shape), lens)
+                n_max, times = measure(spec, args.seed, configs, args.steps, args.warmup,
+                                       args.repeats, args.allocations)
+                calib[f"{b}:{dist}"] = {"batch": b, "dist": dist, "n_max": n_max, "times": times}
+            log(f"  {dist}: {len(SKEWED_BATCHES)} cells timed ({time.time() - t0:.0f} s so far)")
+    for b in ([] if args.skewed else traces.POLICY_BATCHES):
         for n in grid_of(b):
             spec = cell_spec(b, n, args.hq, args.hkv, args.dtype, args.d)
             lens = traces.draw_lengths(spec, np.random.default_rng(args.seed))
@@ -239,7 +275,8 @@ def cmd_measure(args) -> int:
            "device": torch.cuda.get_device_name(0), "repeats": args.repeats,
            "allocations": args.allocations, "calibration": calib,
            "seconds": round(time.time() - t0, 1)}
-    stem = (f"hq{args.hq}_hkv{args.hkv}_{args.dtype}" + (f"_d{args.d}" if args.d != 128 else ""))
+    stem = (f"hq{args.hq}_hkv{args.hkv}_{args.dtype}" + (f"_d{args.d}" if args.d != 128 else "")
+            + ("_skewed" if args.skewed else ""))
     name = f"cost_heldout_{stem}.json" if held_out else f"cost_calib_{stem}.json"
     out = args.out if args.out != engine.COST_MODEL_PATH else os.path.join(
         os.path.dirname(engine.COST_MODEL_PATH), name)
@@ -363,8 +400,9 @@ def evaluate_file(path: str, model_path: str) -> dict:
            **{f"{p}:{s}": 0.0 for p, s in SINGLE_PATHS}}
     worse = {"model": 0, "table": 0, "default": 0}
     for cell in doc["calibration"].values():
-        b, cap, times = cell["batch"], cell["cap"], cell["times"]
-        lens = traces.draw_lengths(cell_spec(b, cap), np.random.default_rng(doc["calibration_seed"]))
+        b, times = cell["batch"], cell["times"]
+        lens = traces.draw_lengths(spec_of_cell(cell, shape),
+                                   np.random.default_rng(doc["calibration_seed"]))
         if int(lens.max()) != cell["n_max"]:
             raise RuntimeError(f"{path}: regenerated lengths differ from the measured ones")
         m_path, m_s, _ = engine.choose_model(model, sweep_problem(b, shape), lens)
@@ -417,6 +455,9 @@ def main(argv=None) -> int:
                     help="measure, check: interleaved timed repeats per placement")
     ap.add_argument("--allocations", type=int, default=ALLOCATIONS,
                     help="measure, check: placements of each cell's buffers in memory")
+    ap.add_argument("--skewed", action="store_true",
+                    help="measure: bimodal and Zipf length mixes at B in "
+                         f"{SKEWED_BATCHES} instead of the (B, N_max) grid")
     args = ap.parse_args(argv)
     return {"measure": cmd_measure, "fit": cmd_fit, "check": cmd_check,
             "evaluate": cmd_evaluate}[args.cmd](args)

@@ -85,7 +85,8 @@ def test_recorded_shape_checks():
 
 
 @pytest.mark.parametrize("name", ["cost_heldout_hq32_hkv2_f16.json",
-                                  "cost_heldout_hq32_hkv8_f16_d64.json"])
+                                  "cost_heldout_hq32_hkv8_f16_d64.json",
+                                  "cost_heldout_hq32_hkv8_f16_skewed.json"])
 def test_recorded_shape_checks_follow_from_the_stored_timings(name):
     """Scoring the stored held-out timings again (model and table choices
     through the C ABI) reproduces the recorded shape check exactly."""
