@@ -267,6 +267,9 @@ pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void*
  *        f4 sums over the launches the largest page total of one CU
  *   f5 = grid items of all split launches / 1000
  *   f6 = non-empty tasks / 1000
+ *   f7 = pages of the largest task / 100 (WORKQUEUE: min(granule, T_max);
+ *        bucket paths: the largest min(granule, longest row) over the
+ *        buckets; NOSPLIT: T_max)
  * with the counters pkv_plan would report, and the model predicts the step
  * time in microseconds as sum_j weights[path][j] * f_j.  pkv_policy_model
  * returns the candidate with the smallest prediction (the first one on a
@@ -284,7 +287,7 @@ pkv_status pkv_merge(const pkv_problem* prob, const void* plan_host, const void*
  * [1, 65535]), PKV_ESHAPE, PKV_EDTYPE, PKV_ERANGE (a length outside
  * [0, max_pages_per_row * P]).
  */
-#define PKV_COST_FEATURES 7
+#define PKV_COST_FEATURES 8
 
 typedef struct pkv_cost_model {
   int32_t n_candidates;

@@ -14,7 +14,8 @@ hand-calibrated thresholds).  The features restate counters of
        split slot) for the bucket paths, empty slots counting 0 pages) are
        dealt to CUs round-robin in grid order, and the launch contributes the
        largest page total of one CU,
-  f5 = grid items / 1000, f6 = non-empty tasks / 1000.
+  f5 = grid items / 1000, f6 = non-empty tasks / 1000,
+  f7 = pages of the largest task / 100 (the whole longest row for no split).
 
 The model predicts microseconds as w[path] . f; the choice is the argmin.
 
@@ -28,7 +29,7 @@ from __future__ import annotations
 from .planner import pages_of, plan
 
 PATH_IDS = {"bucketed": 0, "workqueue": 1, "nosplit": 2, "padded": 3}
-N_FEATURES = 7
+N_FEATURES = 8
 
 
 def launch_grids(seq_lens, num_kv_heads, num_q_heads, head_dim, page_size, splits, path):
@@ -56,8 +57,9 @@ def features(seq_lens, num_kv_heads, num_q_heads, head_dim, page_size, splits, p
         for j, pages in enumerate(grid):
             per_cu[j % num_cus] += pages
         crit += max(per_cu)
+    largest = max((pages for grid in grids for pages in grid), default=0)
     return [1.0, float(p.n_launches), p.kv_bytes / 1e6, p.merge_state_bytes / 1e6, float(crit),
-            sum(len(g) for g in grids) / 1e3, len(p.tasks) / 1e3]
+            sum(len(g) for g in grids) / 1e3, len(p.tasks) / 1e3, largest / 1e2]
 
 
 def predict_us(weights, path: str, f) -> float:

@@ -45,7 +45,7 @@ EXPORTED = ("pkv_plan_bytes", "pkv_plan", "pkv_plan_get_info", "pkv_decode", "pk
             "pkv_policy", "pkv_cost_features", "pkv_policy_model", "pkv_policy_default",
             "pkv_balanced_splits",
             "pkv_noalloc_bytes", "pkv_attend_noalloc", "pkv_status_str")
-PKV_COST_FEATURES = 7
+PKV_COST_FEATURES = 8
 
 
 class PkvError(RuntimeError):

@@ -139,6 +139,7 @@ pkv_status features(const pkv_problem* prob, const int32_t* lens, int32_t path, 
   f[4] = float(crit);
   f[5] = float(double(items) / 1e3);
   f[6] = float(double(c.n_tasks) / 1e3);
+  f[7] = float(double(c.max_task_pages) / 1e2);
   return PKV_OK;
 }
 

@@ -24,12 +24,13 @@ LENS = [300, 17, 300, 0]  # pages 19, 2, 19, 0
 #   padded   : pads 0 / 2 / 32; grids 0 -> 0; pad 2 (pps 1): 1 1 0 0 | 1 1 0 0 -> 2;
 #              pad 32 (pps 8): (8 8 3 0) x 4 -> CU sums 32 32 12 0 -> 32; total 34;
 #              16 tasks; 6 launches; 32 slots
+#   largest task: workqueue 5, bucketed 5 (length 300), nosplit 19, padded 8 (pad 32)
 KV_MB = 617 * 2 * 64 * 2 * 2 / 1e6
 HAND = {
-    "workqueue": [1, 2, KV_MB, 2 * 18 * 2 * 66 * 4 / 1e6, 22, 0.018, 0.018],
-    "bucketed": [1, 6, KV_MB, 2 * 32 * 2 * 66 * 4 / 1e6, 22, 0.032, 0.020],
-    "nosplit": [1, 1, KV_MB, 0, 38, 0.008, 0.006],
-    "padded": [1, 6, KV_MB, 2 * 32 * 2 * 66 * 4 / 1e6, 34, 0.032, 0.016],
+    "workqueue": [1, 2, KV_MB, 2 * 18 * 2 * 66 * 4 / 1e6, 22, 0.018, 0.018, 0.05],
+    "bucketed": [1, 6, KV_MB, 2 * 32 * 2 * 66 * 4 / 1e6, 22, 0.032, 0.020, 0.05],
+    "nosplit": [1, 1, KV_MB, 0, 38, 0.008, 0.006, 0.19],
+    "padded": [1, 6, KV_MB, 2 * 32 * 2 * 66 * 4 / 1e6, 34, 0.032, 0.016, 0.08],
 }
 
 
@@ -48,7 +49,7 @@ def test_c_features_match_hand_computation(path):
 
 def test_empty_batch_features_are_finite():
     f = cost.features([0, 0], 8, 32, 128, 16, 32, "workqueue", 256)
-    assert f == [1.0, 1.0, 0.0, 0.0, 0.0, 0.0, 0.0]
+    assert f == [1.0, 1.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0]
 
 
 def test_oracle_choice_is_the_argmin():
@@ -121,10 +122,10 @@ def test_policy_model_errors():
 #   workqueue 10 + 2 * 2 (launches) + 0.5 * 22 (critical pages)       = 25
 #   nosplit   1 * 38 (critical pages)                                 = 38
 #   padded    1 + 100 * 0.032 (grid items / 1000)                     = 4.2
-HAND_W = [[0, 1, 0, 0, 1, 0, 0],
-          [10, 2, 0, 0, 0.5, 0, 0],
-          [0, 0, 0, 0, 1, 0, 0],
-          [1, 0, 0, 0, 0, 100, 0]]
+HAND_W = [[0, 1, 0, 0, 1, 0, 0, 0],
+          [10, 2, 0, 0, 0.5, 0, 0, 0],
+          [0, 0, 0, 0, 1, 0, 0, 0],
+          [1, 0, 0, 0, 0, 100, 0, 0]]
 HAND_Y = {"bucketed": 28.0, "workqueue": 25.0, "nosplit": 38.0, "padded": 4.2}
 HAND_CANDS = [("workqueue", 4), ("bucketed", 4), ("nosplit", 1), ("padded", 4)]
 
@@ -148,8 +149,8 @@ def test_choice_is_the_hand_worked_argmin():
 def test_choice_tie_goes_to_the_first_candidate():
     # bucketed now predicts 3 + 22 = 25, the workqueue's value; padded 100 + 3.2.
     w = [list(r) for r in HAND_W]
-    w[0] = [3, 0, 0, 0, 1, 0, 0]
-    w[3] = [100, 0, 0, 0, 0, 100, 0]
+    w[0] = [3, 0, 0, 0, 1, 0, 0, 0]
+    w[3] = [100, 0, 0, 0, 0, 100, 0, 0]
     assert cost.choose(w, HAND_CANDS, LENS, 2, 4, 64, 16, 4)[:2] == ("workqueue", 4)
     swapped = [HAND_CANDS[1], HAND_CANDS[0]] + HAND_CANDS[2:]
     assert cost.choose(w, swapped, LENS, 2, 4, 64, 16, 4)[:2] == ("bucketed", 4)
@@ -237,8 +238,8 @@ def test_default_policy_takes_a_balanced_cap():
     cap for 1 task per CU does not exist (6 > 4 tasks at S = 1)."""
     from oracle import policy
 
-    w = [[1000, 0, 0, 0, 0, 0, 0], [0, 0, 0, 0, 0, 0, 1000],
-         [1000, 0, 0, 0, 0, 0, 0], [1000, 0, 0, 0, 0, 0, 0]]
+    w = [[1000, 0, 0, 0, 0, 0, 0, 0], [0, 0, 0, 0, 0, 0, 1000, 0],
+         [1000, 0, 0, 0, 0, 0, 0, 0], [1000, 0, 0, 0, 0, 0, 0, 0]]
     rules = [(1, 1 << 30, 0, 1 << 30, "nosplit", 1)]
     assert cost.choose(w, HAND_CANDS, LENS, 2, 4, 64, 16, 4)[:2] == ("workqueue", 4)
     assert policy.choose_default(rules, w, HAND_CANDS, LENS, 2, 4, 64, 16, 4) == \
