@@ -43,9 +43,10 @@ def _check_cell(rec, min_band, name):
     tol = 0.02 / min(rec["repeats_us"][rec["best_single"]] + rec["repeats_us"][rec["policy"]])
     assert abs(band - rec["band"]) <= tol + 1e-4, name
     assert abs(float(np.median(ratios)) - rec["policy_over_best_single"]) <= tol + 1e-4, name
-    # The best single path is the one of the lowest median.
+    # The best single path is one of the lowest median (the stored medians
+    # are rounded to 0.01 us, so two paths with equal plans can tie).
     singles = rec["single_us"]
-    assert rec["best_single"].split(":")[0] == min(singles, key=singles.get), name
+    assert singles[rec["best_single"].split(":")[0]] <= min(singles.values()) + 0.01, name
     assert rec["ok"] and float(np.median(ratios)) <= 1 + band, name
 
 
